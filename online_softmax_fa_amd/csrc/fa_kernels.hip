@@ -1,0 +1,730 @@
+// fa_kernels.hip -- gfx950 kernels for the exact attention forward pass with
+// the online-softmax recurrence.
+//
+// Per query row the kernel carries the running maximum m, the running
+// denominator l and the unnormalised output o~ across key tiles; every tile
+// rescales them by alpha = exp(m_old - m_new) and adds its own terms measured
+// against m_new; one division o~ / l comes at the end.
+//   -- "2.2b: FlashAttention -- Online Softmax", section "The Complete Online
+//      Softmax Algorithm"; "The math of FlashAttention", sections "The
+//      rescaling identity, derived" and "The block-wise update, and the full
+//      algorithm".
+// Many query rows are processed at once: every row is independent ("2.2b",
+// "Scaling to Multiple Queries"), so a tile of queries turns the score block
+// into a small matrix and P.V into a dense product ("The math of
+// FlashAttention", end of "The block-wise update").  Both products run on the
+// CDNA4 matrix cores.
+//
+// Work decomposition (one workgroup = NW waves = 32*NW query rows of one
+// (batch, head)):
+//   - each wave owns 32 query rows for the whole kernel;
+//   - key/value tiles of BN keys are staged in LDS, double-buffered, from
+//     16-byte global loads; V is written transposed (key index fastest) so the
+//     P.V operand reads are contiguous;
+//   - scores are formed transposed, S^T = K . Q^T, with the 32x32 MFMA: lane l
+//     then holds 16 keys of ONE query row (row l % 32), so the row maximum and
+//     row sum are in-lane reductions plus one exchange with lane l ^ 32, and
+//     the score registers are already laid out as the B operand of
+//     O^T += V^T . P^T (no data movement between the two products);
+//   - exp is the hardware exp2 with log2(e) folded into the score scale.
+//
+// MFMA register layout used throughout (32x32 output, 16 fp32 per lane):
+//   lane l, register r  ->  row 8*(r/4) + 4*(l/32) + r%4,  column l%32.
+// Operand layout of v_mfma_f32_32x32x16_bf16: lane l supplies row (A) or
+// column (B) l%32 and the 8 consecutive k-slots 8*(l/32) .. 8*(l/32)+7.
+// Operand layout of v_mfma_f32_32x32x2_f32: lane l supplies row/column l%32
+// and k-slot l/32.
+// The k-slot -> key assignment of a contraction is free as long as both
+// operands use the same one; the P.V products use the one the score layout
+// hands them.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "fa_internal.h"
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+static constexpr float kNegInf = -__builtin_inff();
+static constexpr float kLn2 = 0.693147180559945309f;
+
+// ---------------------------------------------------------------------------
+// Grid mapping.  Workgroups are dispatched round-robin over the 8 XCDs
+// (workgroup g runs on XCD g % 8).  The logical index gives every XCD a
+// contiguous range of work items, ordered head by head, so the query tiles of
+// one (batch, head) run together on one XCD and share its L2 for K and V.
+// Within a head, causal query tiles go longest first.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int logical_tile(int g, int G)
+{
+    const int per = G >> 3, rem = G & 7;
+    const int x = g & 7, j = g >> 3;
+    return x * per + (x < rem ? x : rem) + j;
+}
+
+// Position, inside a 32-key block, of register r of a lane with half h = l/32:
+// key = 8*(r/4) + 4*h + r%4.  kpos(r) is the part that does not depend on h.
+__device__ __forceinline__ constexpr int kpos(int r) { return 8 * (r >> 2) + (r & 3); }
+
+// Visibility bits of the 32 keys of one key block, as seen by this lane: bit
+// kpos(r) set <=> register r holds a visible key.
+//   lim      number of leading keys (from the lane's first key) inside both
+//            the causal limit and N_k, clamped to [0, 32]
+//   kvbits   key-padding bits of the block, already shifted by 4*h
+__device__ __forceinline__ uint32_t prefix_bits(int lim)
+{
+    return lim >= 32 ? 0xffffffffu : (lim <= 0 ? 0u : ((1u << lim) - 1u));
+}
+
+template <int NKB>
+__device__ __forceinline__ void apply_visibility(f32x16 (&s)[NKB], const uint32_t (&vis)[NKB])
+{
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            s[kb][r] = ((vis[kb] >> kpos(r)) & 1u) ? s[kb][r] : kNegInf;
+}
+
+// One step of the recurrence on a tile of raw scores held in s (NKB blocks of
+// 16 per lane).  m_raw / mc: running max (raw score units) and fl(m_raw * c),
+// both -inf while no visible key has been seen; l_part: this lane's share of
+// the running denominator.  Turns s into the weights p and returns alpha.
+// c = scale * log2(e) > 0, so the max of raw scores is the max of scaled ones.
+//
+// "2.2b: FlashAttention -- Online Softmax", "The Complete Online Softmax
+// Algorithm": m_block, m_new = max(m, m_block), scale = exp(m - m_new),
+// P = exp(S - m_new), l = l*scale + sum(P).
+// While every key seen so far is masked, m_new is -inf and exp(m - m_new)
+// would be exp(-inf + inf).  The pages never meet this case; the reading here
+// is that such a tile changes nothing: alpha = 1 on the empty state and every
+// weight is exp2(-inf) = 0 (the exponent base is taken as 0 for the weights).
+// The first tile with a visible key then gets alpha = exp2(-inf) = 0, as the
+// pages' -inf initialisation intends.
+template <int NKB, bool ACCURATE>
+__device__ __forceinline__ float online_step(f32x16 (&s)[NKB], float &m_raw, float &mc,
+                                             float &l_part, float c)
+{
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+
+    const float m_new = fmaxf(m_raw, mx);
+    const bool empty = (m_new == kNegInf);
+    const float base = empty ? 0.0f : m_new;
+    const float mc_new = base * c;
+    // The exponent of alpha must use the same reference as the weights: the
+    // fast path measures every weight against the rounded fl(m*c), so alpha is
+    // exp2(fl(m_old*c) - fl(m_new*c)); the accurate path measures them against
+    // m itself, so alpha is exp2((m_old - m_new)*c), whose difference is exact.
+    const float alpha = empty      ? 1.0f
+                        : ACCURATE ? __builtin_amdgcn_exp2f((m_raw - m_new) * c)
+                                   : __builtin_amdgcn_exp2f(mc - mc_new);
+
+    float sum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            // ACCURATE: (s - m) first, so the row maximum maps to exp2(0) = 1
+            // exactly; otherwise a single fma in the log2 domain.
+            const float e = ACCURATE ? (s[kb][r] - base) * c
+                                     : __builtin_fmaf(s[kb][r], c, -mc_new);
+            const float pv = __builtin_amdgcn_exp2f(e);
+            s[kb][r] = pv;
+            sum += pv;
+        }
+    l_part = l_part * alpha + sum;
+    m_raw = m_new;
+    mc = empty ? kNegInf : mc_new;
+    return alpha;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 kernel
+// ---------------------------------------------------------------------------
+template <int D, int BN, int NW>
+struct Bf16Cfg {
+    static constexpr int BM = 32 * NW;
+    static constexpr int BNA = BN < 32 ? 32 : BN;   // keys allocated per tile
+    static constexpr int NKB = BNA / 32;            // 32-key blocks per tile
+    static constexpr int NT16 = BN < 16 ? 1 : BN / 16;  // 16-key k-steps of P.V
+    static constexpr int KP = D + 8;                // K row pitch, elements
+    static constexpr int VP = BNA + 4;              // V^T row pitch, elements
+    static constexpr int K_ELEMS = BNA * KP;
+    static constexpr int V_ELEMS = D * VP;
+    static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
+    static constexpr int T = NW * 64;
+    static constexpr int K_CHUNKS = BN * D / 8;     // 16-byte chunks of a K tile
+    static constexpr int K_PER_T = (K_CHUNKS + T - 1) / T;
+    static constexpr int V_CHUNKS = (BN / 4) * (D / 8);  // 4 keys x 8 columns
+    static constexpr int V_PER_T = (V_CHUNKS + T - 1) / T;
+    static constexpr size_t LDS_BYTES = 2 * BUF_ELEMS * sizeof(uint16_t);
+};
+
+template <int D, int BN, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 1) void fa_fwd_bf16_kernel(const Params p)
+{
+    using C = Bf16Cfg<D, BN, NW>;
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int l31 = lane & 31;
+    const int h = lane >> 5;
+
+    const int G = gridDim.x;
+    const int L = logical_tile(blockIdx.x, G);
+    const int bh = L / p.n_qt;
+    const int qt = CAUSAL ? (p.n_qt - 1 - L % p.n_qt) : (L % p.n_qt);
+    const int b = bh / p.H;
+    const int q0 = qt * C::BM;
+    const int qw0 = q0 + 32 * w;         // first query row of this wave
+    const int qrow = qw0 + l31;          // this lane's query row
+    const int Nq = p.Nq, Nk = p.Nk;
+
+    const uint16_t *Qg = static_cast<const uint16_t *>(p.q) + (size_t)bh * Nq * D;
+    const uint16_t *Kg = static_cast<const uint16_t *>(p.k) + (size_t)bh * Nk * D;
+    const uint16_t *Vg = static_cast<const uint16_t *>(p.v) + (size_t)bh * Nk * D;
+    const uint8_t *Mg = p.mask ? p.mask + (size_t)b * Nk : nullptr;
+
+    // Q fragments: B operand of S^T = K . Q^T.  k-step kk covers head dims
+    // 16*kk .. 16*kk+15; this lane supplies dims 16*kk + 8*h .. +7 of its row.
+    bf16x8 qf[D / 16];
+    {
+        const int qr = qrow < Nq ? qrow : Nq - 1;
+        const uint16_t *src = Qg + (size_t)qr * D + 8 * h;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            qf[kk] = *reinterpret_cast<const bf16x8 *>(src + 16 * kk);
+    }
+
+    // Number of key tiles this workgroup needs.
+    int n_t = (Nk + BN - 1) / BN;
+    if (CAUSAL) {
+        const int last_q = (q0 + C::BM < Nq ? q0 + C::BM : Nq) - 1;
+        const int need = last_q / BN + 1;
+        n_t = need < n_t ? need : n_t;
+    }
+
+    // Staging registers for the next tile.
+    u32x4 kreg[C::K_PER_T];
+    u32x4 vreg[C::V_PER_T][4];
+
+    auto load_tile = [&](int t) {
+        const int k0 = t * BN;
+#pragma unroll
+        for (int i = 0; i < C::K_PER_T; ++i) {
+            const int ch = tid + i * C::T;
+            if (C::K_CHUNKS % C::T == 0 || ch < C::K_CHUNKS) {
+                const int row = ch / (D / 8), col = ch % (D / 8);
+                int kr = k0 + row;
+                kr = kr < Nk ? kr : Nk - 1;
+                kreg[i] = *reinterpret_cast<const u32x4 *>(Kg + (size_t)kr * D + 8 * col);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < C::V_PER_T; ++i) {
+            const int ch = tid + i * C::T;
+            if (C::V_CHUNKS % C::T == 0 || ch < C::V_CHUNKS) {
+                const int kq = ch % (BN / 4), c8 = ch / (BN / 4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    int kr = k0 + 4 * kq + j;
+                    kr = kr < Nk ? kr : Nk - 1;
+                    vreg[i][j] = *reinterpret_cast<const u32x4 *>(Vg + (size_t)kr * D + 8 * c8);
+                }
+            }
+        }
+    };
+
+    auto store_tile = [&](int buf) {
+        uint16_t *Kl = lds + buf * C::BUF_ELEMS;
+        uint16_t *Vl = Kl + C::K_ELEMS;
+#pragma unroll
+        for (int i = 0; i < C::K_PER_T; ++i) {
+            const int ch = tid + i * C::T;
+            if (C::K_CHUNKS % C::T == 0 || ch < C::K_CHUNKS) {
+                const int row = ch / (D / 8), col = ch % (D / 8);
+                *reinterpret_cast<u32x4 *>(Kl + row * C::KP + 8 * col) = kreg[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < C::V_PER_T; ++i) {
+            const int ch = tid + i * C::T;
+            if (C::V_CHUNKS % C::T == 0 || ch < C::V_CHUNKS) {
+                const int kq = ch % (BN / 4), c8 = ch / (BN / 4);
+                // column j of the 8 loaded columns -> V^T row 8*c8 + j, keys
+                // 4*kq .. 4*kq+3 (four bf16 = 8 bytes)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int wd = j >> 1, sh = (j & 1) * 16;
+                    const uint32_t e0 = (vreg[i][0][wd] >> sh) & 0xffffu;
+                    const uint32_t e1 = (vreg[i][1][wd] >> sh) & 0xffffu;
+                    const uint32_t e2 = (vreg[i][2][wd] >> sh) & 0xffffu;
+                    const uint32_t e3 = (vreg[i][3][wd] >> sh) & 0xffffu;
+                    u32x2 pk;
+                    pk[0] = e0 | (e1 << 16);
+                    pk[1] = e2 | (e3 << 16);
+                    *reinterpret_cast<u32x2 *>(Vl + (8 * c8 + j) * C::VP + 4 * kq) = pk;
+                }
+            }
+        }
+    };
+
+    // Running state.  The lane pair (l, l ^ 32) shares one query row and the
+    // same m; each lane keeps its own partial l over the keys it holds.
+    float m_raw = kNegInf, mc = kNegInf, l_part = 0.0f;
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+
+    const float c = p.c;
+
+    if (n_t > 0) {
+        load_tile(p.reverse ? n_t - 1 : 0);
+        store_tile(0);
+    }
+    __syncthreads();
+
+    for (int it = 0; it < n_t; ++it) {
+        const int t = p.reverse ? (n_t - 1 - it) : it;
+        const int buf = it & 1;
+        const bool has_next = it + 1 < n_t;
+        if (has_next) load_tile(p.reverse ? (n_t - 2 - it) : (it + 1));
+
+        const int k0 = t * BN;
+        // Key-padding bits of this tile (bit i <=> key k0 + i visible).
+        uint64_t kv_lo = ~0ull, kv_hi = ~0ull;
+        if (Mg) {
+            const int j0 = k0 + lane;
+            const bool v0 = lane < BN && j0 < Nk && Mg[j0] != 0;
+            kv_lo = __ballot(v0);
+            if (BN > 64) {
+                const int j1 = j0 + 64;
+                const bool v1 = lane + 64 < BN && j1 < Nk && Mg[j1] != 0;
+                kv_hi = __ballot(v1);
+            }
+        }
+        const bool tile_empty = Mg && kv_lo == 0 && (BN <= 64 || kv_hi == 0);
+        // Keys beyond this wave's last row are all masked under causality.
+        const bool wave_skip = tile_empty || (CAUSAL && k0 > qw0 + 31);
+
+        if (!wave_skip) {
+            const uint16_t *Kl = lds + buf * C::BUF_ELEMS;
+            const uint16_t *Vl = Kl + C::K_ELEMS;
+
+            // S^T = K . Q^T for the tile.
+            f32x16 s[C::NKB];
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
+                        Kl + (32 * kb + l31) * C::KP + 16 * kk + 8 * h);
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
+                }
+
+            // Masks go in before the tile maximum ("The math of
+            // FlashAttention", "Pitfalls in implementing the recurrence").
+            const bool kv_partial = Mg && !(kv_lo == ~0ull && (BN <= 64 || kv_hi == ~0ull));
+            const bool tail = k0 + C::BNA > Nk || BN < 32;
+            const bool diag = CAUSAL && (k0 + BN - 1 > qw0);
+            if (kv_partial || tail || diag) {
+                uint32_t vis[C::NKB];
+#pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb) {
+                    const int first = k0 + 32 * kb + 4 * h;  // key of kpos 0
+                    int lim = (BN < 32 ? k0 + BN : Nk) - first;
+                    if (BN < 32 && Nk - first < lim) lim = Nk - first;
+                    if (CAUSAL && qrow - first + 1 < lim) lim = qrow - first + 1;
+                    // keys are at kpos 0-3, 8-11, 16-19, 24-27 of the lane's
+                    // bit word; a key at kpos k is visible iff its offset from
+                    // `first`, k, is below lim.
+                    uint32_t bits = prefix_bits(lim);
+                    if (Mg) {
+                        const uint64_t word = (kb < 2) ? kv_lo : kv_hi;
+                        const uint32_t kvw = (uint32_t)(word >> (32 * (kb & 1) + 4 * h));
+                        bits &= kvw;
+                    }
+                    vis[kb] = bits;
+                }
+                apply_visibility<C::NKB>(s, vis);
+            }
+
+            const float alpha = online_step<C::NKB, false>(s, m_raw, mc, l_part, c);
+
+            // Rescale o~ only when some row of the wave changed its maximum
+            // ("Rescale if maximum changed").
+            if (__any(alpha != 1.0f)) {
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            }
+
+            // o~ += P . V as O^T += V^T . P^T.  k-step t covers keys
+            // 16t .. 16t+15; this lane's 8 weights are registers 8*(t%2) ..
+            // 8*(t%2)+7 of key block t/2, i.e. keys 16t + 4h + {0..3, 8..11}.
+#pragma unroll
+            for (int t16 = 0; t16 < C::NT16; ++t16) {
+                bf16x8 pb;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pb[i] = (__bf16)s[t16 >> 1][8 * (t16 & 1) + i];
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const uint16_t *row = Vl + (32 * db + l31) * C::VP + 16 * t16 + 4 * h;
+                    const u32x2 lo = *reinterpret_cast<const u32x2 *>(row);
+                    const u32x2 hi = *reinterpret_cast<const u32x2 *>(row + 8);
+                    u32x4 av;
+                    av[0] = lo[0]; av[1] = lo[1]; av[2] = hi[0]; av[3] = hi[1];
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, av), pb, o[db], 0, 0, 0);
+                }
+            }
+        }
+
+        if (has_next) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue: o = o~ / l, lse = m + ln l; a row with no visible key gets
+    // o = 0 and lse = -inf.
+    const float l_row = l_part + __shfl_xor(l_part, 32);
+    const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
+    if (qrow < Nq) {
+        uint16_t *Og = static_cast<uint16_t *>(p.o) + ((size_t)bh * Nq + qrow) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const __bf16 x0 = (__bf16)(o[db][4 * g + 0] * inv);
+                const __bf16 x1 = (__bf16)(o[db][4 * g + 1] * inv);
+                const __bf16 x2 = (__bf16)(o[db][4 * g + 2] * inv);
+                const __bf16 x3 = (__bf16)(o[db][4 * g + 3] * inv);
+                u32x2 pk;
+                pk[0] = (uint32_t)__builtin_bit_cast(uint16_t, x0) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, x1) << 16);
+                pk[1] = (uint32_t)__builtin_bit_cast(uint16_t, x2) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, x3) << 16);
+                *reinterpret_cast<u32x2 *>(Og + 32 * db + 8 * g + 4 * h) = pk;
+            }
+        if (h == 0)
+            p.lse[(size_t)bh * Nq + qrow] =
+                l_row > 0.0f ? (mc + __builtin_amdgcn_logf(l_row)) * kLn2 : kNegInf;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel: same recurrence with fp32 MFMA products and fp32 weights.  It
+// exists for exact-input checks at fp32 precision; K and V keep the
+// [key][dim] layout in LDS (the fp32 operands are one element per lane, so
+// no transposition is needed), single-buffered.
+// ---------------------------------------------------------------------------
+template <int D, int BN, int NW>
+struct F32Cfg {
+    static constexpr int BM = 32 * NW;
+    static constexpr int BNA = BN < 32 ? 32 : BN;
+    static constexpr int NKB = BNA / 32;
+    static constexpr int P = D + 4;                 // row pitch, floats
+    static constexpr int K_ELEMS = BNA * P;
+    static constexpr int T = NW * 64;
+    static constexpr int CHUNKS = BN * D / 4;       // 16-byte chunks per matrix
+    static constexpr int PER_T = (CHUNKS + T - 1) / T;
+    static constexpr size_t LDS_BYTES = 2 * K_ELEMS * sizeof(float);
+};
+
+template <int D, int BN, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 1) void fa_fwd_f32_kernel(const Params p)
+{
+    using C = F32Cfg<D, BN, NW>;
+    extern __shared__ __attribute__((aligned(16))) float ldsf[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int l31 = lane & 31;
+    const int h = lane >> 5;
+
+    const int G = gridDim.x;
+    const int L = logical_tile(blockIdx.x, G);
+    const int bh = L / p.n_qt;
+    const int qt = CAUSAL ? (p.n_qt - 1 - L % p.n_qt) : (L % p.n_qt);
+    const int b = bh / p.H;
+    const int q0 = qt * C::BM;
+    const int qw0 = q0 + 32 * w;
+    const int qrow = qw0 + l31;
+    const int Nq = p.Nq, Nk = p.Nk;
+
+    const float *Qg = static_cast<const float *>(p.q) + (size_t)bh * Nq * D;
+    const float *Kg = static_cast<const float *>(p.k) + (size_t)bh * Nk * D;
+    const float *Vg = static_cast<const float *>(p.v) + (size_t)bh * Nk * D;
+    const uint8_t *Mg = p.mask ? p.mask + (size_t)b * Nk : nullptr;
+
+    // Q fragments: the 4 MFMAs of group g contract dims 8g + 4h + i (i = 0..3)
+    // on this lane, for both operands.
+    f32x4 qf[D / 8];
+    {
+        const int qr = qrow < Nq ? qrow : Nq - 1;
+#pragma unroll
+        for (int g = 0; g < D / 8; ++g)
+            qf[g] = *reinterpret_cast<const f32x4 *>(Qg + (size_t)qr * D + 8 * g + 4 * h);
+    }
+
+    int n_t = (Nk + BN - 1) / BN;
+    if (CAUSAL) {
+        const int last_q = (q0 + C::BM < Nq ? q0 + C::BM : Nq) - 1;
+        const int need = last_q / BN + 1;
+        n_t = need < n_t ? need : n_t;
+    }
+
+    float *Kl = ldsf;
+    float *Vl = ldsf + C::K_ELEMS;
+    f32x4 kreg[C::PER_T], vreg[C::PER_T];
+
+    auto load_tile = [&](int t) {
+        const int k0 = t * BN;
+#pragma unroll
+        for (int i = 0; i < C::PER_T; ++i) {
+            const int ch = tid + i * C::T;
+            if (C::CHUNKS % C::T == 0 || ch < C::CHUNKS) {
+                const int row = ch / (D / 4), col = ch % (D / 4);
+                int kr = k0 + row;
+                kr = kr < Nk ? kr : Nk - 1;
+                kreg[i] = *reinterpret_cast<const f32x4 *>(Kg + (size_t)kr * D + 4 * col);
+                vreg[i] = *reinterpret_cast<const f32x4 *>(Vg + (size_t)kr * D + 4 * col);
+            }
+        }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int i = 0; i < C::PER_T; ++i) {
+            const int ch = tid + i * C::T;
+            if (C::CHUNKS % C::T == 0 || ch < C::CHUNKS) {
+                const int row = ch / (D / 4), col = ch % (D / 4);
+                *reinterpret_cast<f32x4 *>(Kl + row * C::P + 4 * col) = kreg[i];
+                *reinterpret_cast<f32x4 *>(Vl + row * C::P + 4 * col) = vreg[i];
+            }
+        }
+    };
+
+    float m_raw = kNegInf, mc = kNegInf, l_part = 0.0f;
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+
+    const float c = p.c;
+
+    // Phantom keys of a 16-key tile (rows 16..31 of the 32-row block) are
+    // never written; zero them once so the P.V products read finite values.
+    if (BN < 32) {
+        for (int x = tid; x < (C::BNA - BN) * C::P; x += C::T) {
+            Kl[BN * C::P + x] = 0.0f;
+            Vl[BN * C::P + x] = 0.0f;
+        }
+    }
+
+    if (n_t > 0) load_tile(p.reverse ? n_t - 1 : 0);
+
+    for (int it = 0; it < n_t; ++it) {
+        const int t = p.reverse ? (n_t - 1 - it) : it;
+        __syncthreads();   // every wave is done with the previous tile
+        store_tile();
+        __syncthreads();
+        if (it + 1 < n_t) load_tile(p.reverse ? (n_t - 2 - it) : (it + 1));
+
+        const int k0 = t * BN;
+        uint64_t kv_lo = ~0ull, kv_hi = ~0ull;
+        if (Mg) {
+            const int j0 = k0 + lane;
+            const bool v0 = lane < BN && j0 < Nk && Mg[j0] != 0;
+            kv_lo = __ballot(v0);
+            if (BN > 64) {
+                const int j1 = j0 + 64;
+                const bool v1 = lane + 64 < BN && j1 < Nk && Mg[j1] != 0;
+                kv_hi = __ballot(v1);
+            }
+        }
+        const bool tile_empty = Mg && kv_lo == 0 && (BN <= 64 || kv_hi == 0);
+        if (tile_empty || (CAUSAL && k0 > qw0 + 31)) continue;
+
+        f32x16 s[C::NKB];
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+#pragma unroll
+        for (int g = 0; g < D / 8; ++g)
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb) {
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(
+                    Kl + (32 * kb + l31) * C::P + 8 * g + 4 * h);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], qf[g][i], s[kb], 0, 0, 0);
+            }
+
+        const bool kv_partial = Mg && !(kv_lo == ~0ull && (BN <= 64 || kv_hi == ~0ull));
+        const bool tail = k0 + C::BNA > Nk || BN < 32;
+        const bool diag = CAUSAL && (k0 + BN - 1 > qw0);
+        if (kv_partial || tail || diag) {
+            uint32_t vis[C::NKB];
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb) {
+                const int first = k0 + 32 * kb + 4 * h;
+                int lim = (BN < 32 ? k0 + BN : Nk) - first;
+                if (BN < 32 && Nk - first < lim) lim = Nk - first;
+                if (CAUSAL && qrow - first + 1 < lim) lim = qrow - first + 1;
+                uint32_t bits = prefix_bits(lim);
+                if (Mg) {
+                    const uint64_t word = (kb < 2) ? kv_lo : kv_hi;
+                    bits &= (uint32_t)(word >> (32 * (kb & 1) + 4 * h));
+                }
+                vis[kb] = bits;
+            }
+            apply_visibility<C::NKB>(s, vis);
+        }
+
+        const float alpha = online_step<C::NKB, true>(s, m_raw, mc, l_part, c);
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        }
+
+        // O^T += V^T . P^T: the MFMA fed by weight register r contracts over
+        // the two keys 32kb + kpos(r) (lanes 0-31) and 32kb + kpos(r) + 4
+        // (lanes 32-63); the V operand of lane l is V[that key][32db + l%32].
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                // keys 16..31 of a 16-key tile are phantoms (registers 8..15)
+                if (BN < 32 && r >= 8) continue;
+                const int key = 32 * kb + kpos(r) + 4 * h;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const float a = Vl[key * C::P + 32 * db + l31];
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[kb][r], o[db], 0, 0, 0);
+                }
+            }
+    }
+
+    const float l_row = l_part + __shfl_xor(l_part, 32);
+    const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
+    if (qrow < Nq) {
+        float *Og = static_cast<float *>(p.o) + ((size_t)bh * Nq + qrow) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 x;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[i] = o[db][4 * g + i] * inv;
+                *reinterpret_cast<f32x4 *>(Og + 32 * db + 8 * g + 4 * h) = x;
+            }
+        if (h == 0)
+            p.lse[(size_t)bh * Nq + qrow] =
+                l_row > 0.0f ? __builtin_fmaf(m_raw, p.scale, __builtin_amdgcn_logf(l_row) * kLn2)
+                             : kNegInf;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+// Dynamic LDS above the default limit is opted into once per kernel and
+// device.
+template <auto Kernel>
+static hipError_t launch(int grid, int threads, size_t lds, hipStream_t stream, const Params &p)
+{
+    static std::atomic<uint64_t> attr_done{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = 1ull << (dev & 63);
+    if (!(attr_done.load(std::memory_order_acquire) & bit)) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(Kernel),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr_done.fetch_or(bit, std::memory_order_acq_rel);
+    }
+    hipLaunchKernelGGL(Kernel, dim3(grid), dim3(threads), lds, stream, p);
+    return hipGetLastError();
+}
+
+template <int D, int BN>
+static hipError_t dispatch_bf16(const Params &p0, int causal, int B, int H, hipStream_t stream)
+{
+    constexpr int NW = 4;
+    using C = Bf16Cfg<D, BN, NW>;
+    Params p = p0;
+    p.n_qt = (p.Nq + C::BM - 1) / C::BM;
+    const int grid = B * H * p.n_qt;
+    if (causal)
+        return launch<fa_fwd_bf16_kernel<D, BN, NW, true>>(grid, C::T, C::LDS_BYTES, stream, p);
+    return launch<fa_fwd_bf16_kernel<D, BN, NW, false>>(grid, C::T, C::LDS_BYTES, stream, p);
+}
+
+template <int D, int BN>
+static hipError_t dispatch_f32(const Params &p0, int causal, int B, int H, hipStream_t stream)
+{
+    constexpr int NW = 4;
+    using C = F32Cfg<D, BN, NW>;
+    Params p = p0;
+    p.n_qt = (p.Nq + C::BM - 1) / C::BM;
+    const int grid = B * H * p.n_qt;
+    if (causal)
+        return launch<fa_fwd_f32_kernel<D, BN, NW, true>>(grid, C::T, C::LDS_BYTES, stream, p);
+    return launch<fa_fwd_f32_kernel<D, BN, NW, false>>(grid, C::T, C::LDS_BYTES, stream, p);
+}
+
+template <int D>
+static hipError_t dispatch_d(const Params &p, int dtype, int block_n, int causal, int B, int H,
+                             hipStream_t s)
+{
+    if (dtype == 1) {
+        switch (block_n) {
+        case 16: return dispatch_bf16<D, 16>(p, causal, B, H, s);
+        case 32: return dispatch_bf16<D, 32>(p, causal, B, H, s);
+        case 128: return dispatch_bf16<D, 128>(p, causal, B, H, s);
+        default: return dispatch_bf16<D, 64>(p, causal, B, H, s);
+        }
+    }
+    switch (block_n) {
+    case 16: return dispatch_f32<D, 16>(p, causal, B, H, s);
+    case 32: return dispatch_f32<D, 32>(p, causal, B, H, s);
+    case 128: return dispatch_f32<D, 128>(p, causal, B, H, s);
+    default: return dispatch_f32<D, 64>(p, causal, B, H, s);
+    }
+}
+
+hipError_t launch_fwd(const Params &p, int dtype, int d, int block_n, int causal, int B, int H,
+                      hipStream_t stream)
+{
+    if (d == 64) return dispatch_d<64>(p, dtype, block_n, causal, B, H, stream);
+    return dispatch_d<128>(p, dtype, block_n, causal, B, H, stream);
+}
+
+}  // namespace fa

@@ -1,0 +1,118 @@
+"""The C-ABI boundary, checked without a GPU: the library loads, exports every
+entry point include/fa.h declares, rejects bad arguments with the documented
+codes before touching any device, and stays independent of the oracle."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+import online_softmax_fa_amd as fa  # noqa: E402
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        pytest.fail("libfa.so is not built; run __graft_entry__.build()")
+    return fa.load_library()
+
+
+def test_header_declares_the_entry_points():
+    assert _declared_functions() == ["fa_fwd", "fa_fwd_ex", "fa_strerror"]
+
+
+def test_header_compiles_as_c_and_cxx(tmp_path):
+    src = tmp_path / "use.c"
+    src.write_text('#include "fa.h"\nint main(void){fa_opts o={0,0};(void)o;'
+                   'return fa_fwd(0,0,0,0,0,1,1,1,1,64,1.0f,0,0,FA_DTYPE_BF16,0)==FA_ERR_NULL?0:1;}\n')
+    for comp, std in (("gcc", "-std=c99"), ("g++", "-std=c++17")):
+        subprocess.run([comp, std, "-fsyntax-only", "-Wall", "-Werror", "-I",
+                        os.path.join(ROOT, "include"), "-x", "c" if comp == "gcc" else "c++",
+                        str(src)], check=True)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (fa_\w+)", out))
+    assert set(_declared_functions()) <= exported
+
+
+def test_strerror_covers_every_code(lib):
+    for code in range(0, -10, -1):
+        s = fa.fa_strerror(code)
+        assert s and s != "unknown status code", code
+    assert fa.fa_strerror(-99) == "unknown status code"
+
+
+FAKE = 0x10000          # never dereferenced: validation fails first
+FAKE2 = 0x20000000
+FAKE3 = 0x40000000
+FAKE4 = 0x60000000
+FAKE5 = 0x80000000
+
+
+def _call(q=FAKE, k=FAKE2, v=FAKE3, o=FAKE4, lse=FAKE5, B=1, H=1, Nq=8, Nk=8, d=64, scale=0.125,
+          causal=0, mask=None, dtype=1, block_n=0):
+    lib = fa.load_library()
+    opts = fa.fa_opts(block_n, 0)
+    return lib.fa_fwd_ex(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, mask, dtype, None,
+                         ctypes.byref(opts))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), fa.FA_ERR_NULL), (dict(k=None), fa.FA_ERR_NULL), (dict(v=None), fa.FA_ERR_NULL),
+    (dict(o=None), fa.FA_ERR_NULL), (dict(lse=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(H=-1), fa.FA_ERR_SHAPE), (dict(Nq=0), fa.FA_ERR_SHAPE),
+    (dict(Nk=0), fa.FA_ERR_SHAPE), (dict(B=1 << 20, H=1 << 20, Nq=1 << 20), fa.FA_ERR_SHAPE),
+    (dict(d=96), fa.FA_ERR_HEAD_DIM), (dict(d=256), fa.FA_ERR_HEAD_DIM),
+    (dict(dtype=2), fa.FA_ERR_DTYPE), (dict(dtype=-1), fa.FA_ERR_DTYPE),
+    (dict(scale=0.0), fa.FA_ERR_SCALE), (dict(scale=-0.5), fa.FA_ERR_SCALE),
+    (dict(scale=float("nan")), fa.FA_ERR_SCALE), (dict(scale=float("inf")), fa.FA_ERR_SCALE),
+    (dict(block_n=48), fa.FA_ERR_TILE), (dict(block_n=256), fa.FA_ERR_TILE),
+    (dict(o=FAKE), fa.FA_ERR_ALIAS), (dict(lse=FAKE3 + 16), fa.FA_ERR_ALIAS),
+    (dict(mask=FAKE4 + 1), fa.FA_ERR_ALIAS),
+])
+def test_argument_errors_before_any_device_work(lib, kw, code):
+    assert _call(**kw) == code
+
+
+def test_valid_arguments_without_gpu_report_device_error(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _call() == fa.FA_ERR_DEVICE
+
+
+def test_binding_raises_with_the_message(lib):
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_fwd_ex(FAKE, FAKE2, FAKE3, FAKE4, FAKE5, 1, 1, 8, 8, 100, 0.125, 0, None, 1, None)
+    assert e.value.code == fa.FA_ERR_HEAD_DIM and "64 or 128" in str(e.value)
+
+
+def test_product_path_is_independent_of_the_oracle():
+    """Neither the library sources nor the binding refer to the oracle, and the
+    built library links no oracle code."""
+    pkg = os.path.join(ROOT, "online_softmax_fa_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "ref_attn" not in text and "libfaref" not in text, f
+    out = subprocess.run(["objdump", "-p", fa.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    assert "faref" not in out

@@ -1,0 +1,267 @@
+"""GPU parity: the HIP path (through the C ABI binding) against the fp64 oracle
+on the same seeded inputs, element by element.
+
+Workloads (online_softmax_fa_amd.inputs): the small fp32 case and the pages'
+toy rows; the adversarial exact-score heads with every mask case, both
+dtypes, every tile size and both traversal orders; the mid-size causal bf16
+case; the headline causal bf16 case and the long-context case on sampled rows
+(at the launch configuration the bench times); and edge shapes (ragged tails,
+one key, one query, fully masked rows and batches).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from online_softmax_fa_amd import inputs
+from _parity import compare, run_gpu, run_oracle, sample_rows, say, to_np32
+
+pytestmark = pytest.mark.gpu
+
+BLOCKS = (16, 32, 64, 128)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import online_softmax_fa_amd as fa
+    fa.load_library()
+    props = torch.cuda.get_device_properties(0)
+    say("device: %s %s" % (props.name, getattr(props, "gcnArchName", "")))
+
+
+# ---------------------------------------------------------------------------
+def test_small_fp32():
+    w = inputs.workload("small")
+    say("small fp32 B=1 H=1 N=256 d=64")
+    o, lse = run_gpu(w["q"], w["k"], w["v"], w["scale"])
+    o_ref, lse_ref = run_oracle(w["q"], w["k"], w["v"], w["scale"])
+    compare(o, lse, o_ref, lse_ref, "f32", what="small")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_small_all_tiles_agree(dtype):
+    w = inputs.workload("small", dtype=dtype)
+    o_ref, lse_ref = run_oracle(w["q"], w["k"], w["v"], w["scale"])
+    outs = []
+    for bn in BLOCKS:
+        for rev in (False, True):
+            say("small %s block_n=%d reverse=%d" % (dtype, bn, rev))
+            o, lse = run_gpu(w["q"], w["k"], w["v"], w["scale"], block_n=bn, reverse_kv=rev)
+            compare(o, lse, o_ref, lse_ref, dtype, what="bn%d rev%d" % (bn, rev))
+            outs.append(o)
+    bar = 1e-5 if dtype == "f32" else 2e-2
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) <= bar
+
+
+def _toy_tensors(scores, values, d=64):
+    """A precomputed score row fed through the library: one query q = e0 and
+    keys k_j = s_j e0 with scale 1, so every score is exact; values occupy the
+    first columns."""
+    n = len(scores)
+    q = torch.zeros(1, 1, 1, d)
+    q[0, 0, 0, 0] = 1.0
+    k = torch.zeros(1, 1, n, d)
+    k[0, 0, :, 0] = torch.tensor(scores, dtype=torch.float32)
+    v = torch.zeros(1, 1, n, d)
+    vals = torch.tensor(values, dtype=torch.float32).reshape(n, -1)
+    v[0, 0, :, :vals.shape[1]] = vals
+    return q, k, v
+
+
+@pytest.mark.parametrize("bn", BLOCKS)
+def test_pages_toy_rows(bn):
+    """'2.2b', 'The Softmax Formula' (S=[2,4,1,3] -> [0.087, 0.644, 0.032,
+    0.237]); 'The math of FlashAttention', 'A fully worked numeric example'
+    (s=[1,3,2,5], v=[10,20,30,40] -> 36.88)."""
+    q, k, v = _toy_tensors([2, 4, 1, 3], np.eye(4))
+    o, lse = run_gpu(q, k, v, 1.0, block_n=bn)
+    assert np.max(np.abs(o[0, 0, 0, :4] - np.array([0.087, 0.644, 0.032, 0.237]))) <= 5e-4
+    assert np.all(o[0, 0, 0, 4:] == 0.0)
+    assert abs(math.exp(lse[0, 0, 0]) - 84.80) <= 0.02
+    o_ref, lse_ref = run_oracle(q, k, v, 1.0)
+    compare(o, lse, o_ref, lse_ref, "f32", what="toy1 bn%d" % bn)
+
+    q, k, v = _toy_tensors([1, 3, 2, 5], [[10], [20], [30], [40]])
+    o, lse = run_gpu(q, k, v, 1.0, block_n=bn)
+    assert abs(o[0, 0, 0, 0] - 36.88) <= 5e-3
+    o_ref, lse_ref = run_oracle(q, k, v, 1.0)
+    compare(o, lse, o_ref, lse_ref, "f32", max_abs=1e-5 * 40, what="toy2 bn%d" % bn)
+
+    q, k, v = _toy_tensors([1, 2, 5, 3], [[1, 0], [0, 1], [2, 0], [0, 2]])
+    o, lse = run_gpu(q, k, v, 1.0, block_n=bn)
+    assert np.max(np.abs(o[0, 0, 0, :2] - np.array([1.677, 0.266]))) <= 5e-4
+
+
+# ---------------------------------------------------------------------------
+# Adversarial heads: exact scores, max in the last / first tile, max jumps that
+# underflow alpha, maxima straddling ln(FLT_MAX), key-padding masks, fully
+# masked rows; every tile size and both traversal orders.
+# ---------------------------------------------------------------------------
+ADV_CASES = list(inputs.adversarial_cases().keys())
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", ADV_CASES)
+def test_adversarial(dtype, case):
+    q, k, v = inputs.adversarial(dtype=dtype)
+    mask, causal = inputs.adversarial_cases()[case]
+    say("adversarial %s %s causal=%d" % (dtype, case, causal))
+    o_ref, lse_ref = run_oracle(q, k, v, inputs.ADV_SCALE, causal=causal, mask=mask)
+    outs = []
+    for bn in BLOCKS:
+        for rev in (False, True):
+            o, lse = run_gpu(q, k, v, inputs.ADV_SCALE, causal=causal, mask=mask, block_n=bn,
+                             reverse_kv=rev)
+            compare(o, lse, o_ref, lse_ref, dtype, what="%s bn%d rev%d" % (case, bn, rev))
+            outs.append(o)
+    bar = 1e-5 if dtype == "f32" else 2e-2
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) <= bar
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_adversarial_random_scaled(dtype):
+    """Gaussian Q, K scaled so |scores| reach about 80.  bf16 is held to the
+    bf16 bar.  For fp32 the scores themselves carry fp32 rounding before any
+    softmax arithmetic: with |delta s_j| <= d * 2^-24 * scale * sum_c |q_c k_jc|
+    (a bound on any fp32 dot-product order), the output moves by at most
+    2 * max_j |delta s_j| * max |v| (first order), so that bound (plus 1e-5) is
+    the fp32 bar for this case."""
+    q, k, v = inputs.adversarial_random(dtype=dtype)
+    o_ref, lse_ref = run_oracle(q, k, v, inputs.ADV_SCALE)
+    if dtype == "f32":
+        qa, ka = np.abs(to_np32(q)).astype(np.float64), np.abs(to_np32(k)).astype(np.float64)
+        worst = (qa @ np.swapaxes(ka, -1, -2)).max() * inputs.ADV_SCALE
+        ds = 64 * 2.0 ** -24 * worst
+        bar = 1e-5 + 2 * ds * np.abs(to_np32(v)).max()
+        lse_bar = max(1e-3, 2 * ds)
+    else:
+        bar, lse_bar = None, 1e-3
+    say("adversarial random-scaled %s: fp32 bar %s" % (dtype, bar))
+    s_max = float(np.abs(np.asarray(lse_ref)).max())
+    assert s_max > 40.0            # the case really reaches large logits
+    for bn in (32, 64, 128):
+        o, lse = run_gpu(q, k, v, inputs.ADV_SCALE, block_n=bn)
+        compare(o, lse, o_ref, lse_ref, dtype, max_abs=bar, lse_tol=lse_bar, what="bn%d" % bn)
+
+
+# ---------------------------------------------------------------------------
+# Edge shapes: ragged tails on both sides, one key, one query, d = 128 in fp32
+# ---------------------------------------------------------------------------
+EDGE = [
+    # (B, H, Nq, Nk, d, causal, masked)
+    (1, 1, 1, 1, 64, False, False),
+    (1, 2, 1, 4, 64, False, False),
+    (2, 3, 33, 33, 64, True, False),
+    (1, 2, 100, 37, 128, False, True),
+    (1, 2, 37, 100, 128, True, True),
+    (2, 1, 257, 300, 64, False, True),
+    (1, 1, 129, 1, 128, False, False),
+    (1, 3, 300, 257, 128, True, False),
+    (3, 2, 64, 64, 64, True, True),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", EDGE, ids=["x".join(map(str, s[:5])) + ("c" if s[5] else "")
+                                             + ("m" if s[6] else "") for s in EDGE])
+def test_edge_shapes(dtype, shape):
+    B, H, Nq, Nk, d, causal, masked = shape
+    seed = 5000 + Nq * 7 + Nk
+    q, k, v = inputs.gaussian_qkv(B, H, Nq, Nk, d, seed, 1.0, dtype)
+    mask = None
+    if masked:
+        mask = inputs.bernoulli_mask(B, Nk, 0.3, seed + 1)
+        mask[0, : min(5, Nk)] = 0
+    scale = inputs.default_scale(d)
+    o_ref, lse_ref = run_oracle(q, k, v, scale, causal=causal, mask=mask)
+    for bn in (16, 64, 128):
+        say("edge %s %s bn=%d" % (dtype, shape, bn))
+        o, lse = run_gpu(q, k, v, scale, causal=causal, mask=mask, block_n=bn)
+        compare(o, lse, o_ref, lse_ref, dtype, what="bn%d" % bn)
+
+
+def test_fully_masked_batch_and_rows():
+    B, H, N, d = 3, 2, 96, 64
+    q, k, v = inputs.gaussian_qkv(B, H, N, N, d, 77, 1.0, "bf16")
+    mask = torch.ones(B, N, dtype=torch.uint8)
+    mask[0] = 0                 # batch 0: no key at all
+    mask[1, :50] = 0            # batch 1 causal: rows 0..49 see nothing
+    o, lse = run_gpu(q, k, v, 0.125, causal=True, mask=mask)
+    o_ref, lse_ref = run_oracle(q, k, v, 0.125, causal=True, mask=mask)
+    assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))
+    assert np.all(o[1, :, :50] == 0) and np.all(np.isneginf(lse[1, :, :50]))
+    compare(o, lse, o_ref, lse_ref, "bf16", what="masked batch")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_weights_sum_to_one_and_causal_row0(dtype):
+    """A constant value column comes back unchanged (the weights sum to 1);
+    causal row 0 sees only key 0, so o = v_0 exactly."""
+    B, H, N, d = 2, 4, 200, 128
+    q, k, v = inputs.gaussian_qkv(B, H, N, N, d, 88, 2.0, dtype)
+    v[..., 5] = 1.0
+    o, lse = run_gpu(q, k, v, inputs.default_scale(d), causal=True)
+    # bf16: the weights are rounded to bf16 for the product while l sums them
+    # in fp32, and o is rounded to bf16: within one bf16 step below 1.  fp32:
+    # l and the product sum the same n weights in two different fp32 orders,
+    # each within (n - 1) * 2^-24 relative, so n * 2^-23 bounds the difference.
+    tol = 2.0 ** -8 if dtype == "bf16" else N * 2.0 ** -23
+    assert np.max(np.abs(o[..., 5] - 1.0)) <= tol
+    v0 = to_np32(v)[:, :, 0, :].astype(np.float64)
+    assert np.array_equal(o[:, :, 0, :], v0)
+
+
+# ---------------------------------------------------------------------------
+# Larger workloads
+# ---------------------------------------------------------------------------
+def test_mid_causal_bf16_and_determinism():
+    w = inputs.workload("mid")
+    say("mid bf16 causal B=4 H=16 N=2048 d=64")
+    q, k, v = w["q"], w["k"], w["v"]
+    o, lse = run_gpu(q, k, v, w["scale"], causal=True)
+    heads = [(0, 0), (1, 5), (2, 10), (3, 15)]
+    rows = sample_rows(4, 16, 2048, heads, 256, 11)
+    # two heads in full
+    full = np.concatenate([np.arange(2048) + (b * 16 + h) * 2048 for (b, h) in [(0, 1), (3, 14)]])
+    rows = np.unique(np.concatenate([rows, full]))
+    o_ref, lse_ref = run_oracle(q, k, v, w["scale"], causal=True, rows=rows)
+    compare(o.reshape(-1, 64)[rows], lse.reshape(-1)[rows], o_ref, lse_ref, "bf16", what="mid")
+    o2, lse2 = run_gpu(q, k, v, w["scale"], causal=True)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2), "run-to-run difference"
+
+
+def test_headline_sampled():
+    w = inputs.workload("headline")
+    say("headline bf16 causal B=2 H=32 N=8192 d=128 (sampled rows)")
+    q, k, v = w["q"], w["k"], w["v"]
+    o, lse = run_gpu(q, k, v, w["scale"], causal=True)
+    heads = [(0, 0), (0, 13), (1, 7), (1, 31)]
+    rows = sample_rows(2, 32, 8192, heads, 128, 12)
+    o_ref, lse_ref = run_oracle(q, k, v, w["scale"], causal=True, rows=rows)
+    compare(o.reshape(-1, 128)[rows], lse.reshape(-1)[rows], o_ref, lse_ref, "bf16",
+            what="headline")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+@pytest.mark.parametrize("masked", [False, True])
+def test_long_sampled(masked):
+    w = inputs.workload("long")
+    q, k, v = w["q"], w["k"], w["v"]
+    mask = None
+    if masked:
+        lens = inputs.kv_lengths(1, 32768, 2005)
+        mask = inputs.prefix_mask(lens, 32768)
+        say("long bf16 B=1 H=8 N=32768 d=128, kv length %d" % int(lens[0]))
+    else:
+        say("long bf16 B=1 H=8 N=32768 d=128")
+    o, lse = run_gpu(q, k, v, w["scale"], mask=mask)
+    rows = sample_rows(1, 8, 32768, [(0, 0), (0, 5)], 64, 13)
+    o_ref, lse_ref = run_oracle(q, k, v, w["scale"], mask=mask, rows=rows)
+    compare(o.reshape(-1, 128)[rows], lse.reshape(-1)[rows], o_ref, lse_ref, "bf16",
+            what="long masked=%d" % masked)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
