@@ -154,263 +154,311 @@ __device__ __forceinline__ float online_step(f32x16 (&s)[NKB], float &m_raw, flo
 // ---------------------------------------------------------------------------
 // bf16 kernel
 // ---------------------------------------------------------------------------
+// LDS layout of one pipeline stage: the K tile, then the V tile, each
+// BNA rows of D bf16 (D*2 bytes, unpadded), both in [key][dim] order.  Tiles
+// are filled by LDS DMA (global_load_lds_dwordx4): one wave instruction
+// writes 1 KiB of contiguous LDS, so rows cannot be padded; instead the
+// 16-byte chunks of each row are XOR-permuted (swz_k, swz_v) and every lane
+// loads the global chunk that belongs at its LDS slot.  The permutations keep
+// the two LDS read patterns free of bank conflicts:
+//   K (ds_read_b128): 32 consecutive rows, one 16-byte chunk each;
+//   V (ds_read_b64_tr_b16): per half wave, 4 consecutive rows x 64 bytes.
+template <int D>
+__device__ __forceinline__ int swz_k(int r)
+{
+    if (D == 128) return r & 15;
+    return ((r >> 1) & 7) ^ ((r & 1) << 2);
+}
+
+template <int D>
+__device__ __forceinline__ int swz_v(int r)
+{
+    if (D == 128) return (0xAC60 >> (4 * (r & 3))) & 15;   // 0, 6, 12, 10
+    return 2 * (r & 3);
+}
+
 template <int D, int BN, int NW>
 struct Bf16Cfg {
     static constexpr int BM = 32 * NW;
-    static constexpr int BNA = BN < 32 ? 32 : BN;   // keys allocated per tile
-    static constexpr int NKB = BNA / 32;            // 32-key blocks per tile
-    static constexpr int NT16 = BN < 16 ? 1 : BN / 16;  // 16-key k-steps of P.V
-    static constexpr int KP = D + 8;                // K row pitch, elements
-    static constexpr int VP = BNA + 4;              // V^T row pitch, elements
-    static constexpr int K_ELEMS = BNA * KP;
-    static constexpr int V_ELEMS = D * VP;
-    static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
+    static constexpr int BNA = BN < 32 ? 32 : BN;        // key rows allocated per tile
+    static constexpr int NKB = BNA / 32;                 // 32-key blocks per tile
+    static constexpr int NT16 = BN / 16;                 // 16-key k-steps of P.V
+    static constexpr int ROW = D * 2;                    // bytes per key row
+    static constexpr int CH = ROW / 16;                  // 16-byte chunks per row
+    static constexpr int TILE = BNA * ROW;               // bytes of one K or V tile
+    static constexpr int STAGE = 2 * TILE;
+    static constexpr size_t LDS_BYTES = 2 * STAGE;
+    static constexpr int ROWS_PER_DMA = 1024 / ROW;
+    static constexpr int DMA_PER_TILE = BN * ROW / 1024;  // wave instructions per matrix
+    static constexpr int DMA_PER_WAVE = (DMA_PER_TILE + NW - 1) / NW;
     static constexpr int T = NW * 64;
-    static constexpr int K_CHUNKS = BN * D / 8;     // 16-byte chunks of a K tile
-    static constexpr int K_PER_T = (K_CHUNKS + T - 1) / T;
-    static constexpr int V_CHUNKS = (BN / 4) * (D / 8);  // 4 keys x 8 columns
-    static constexpr int V_PER_T = (V_CHUNKS + T - 1) / T;
-    static constexpr size_t LDS_BYTES = 2 * BUF_ELEMS * sizeof(uint16_t);
 };
 
+// s_waitcnt vmcnt(0): every vector-memory operation of this wave, LDS DMA
+// included, has completed (expcnt and lgkmcnt fields left at their maximum).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int N>
+struct IntC {
+    static constexpr int value = N;
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+
+// Per-thread state and steps of the bf16 kernel.  The kernel body is a
+// struct with device member functions (no lambdas), all inlined.
 template <int D, int BN, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 1) void fa_fwd_bf16_kernel(const Params p)
-{
+struct Bf16Fwd {
     using C = Bf16Cfg<D, BN, NW>;
-    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int w = tid >> 6;
-    const int l31 = lane & 31;
-    const int h = lane >> 5;
+    lds_char *lds;
+    int lane, w, l31, h;
+    int bh, b, q0, qw0, qrow, Nq, Nk, n_t;
+    bool reverse;
+    float c;
+    const uint16_t *Kg, *Vg;
+    const uint8_t *Mg;
 
-    const int G = gridDim.x;
-    const int L = logical_tile(blockIdx.x, G);
-    const int bh = L / p.n_qt;
-    const int qt = CAUSAL ? (p.n_qt - 1 - L % p.n_qt) : (L % p.n_qt);
-    const int b = bh / p.H;
-    const int q0 = qt * C::BM;
-    const int qw0 = q0 + 32 * w;         // first query row of this wave
-    const int qrow = qw0 + l31;          // this lane's query row
-    const int Nq = p.Nq, Nk = p.Nk;
-
-    const uint16_t *Qg = static_cast<const uint16_t *>(p.q) + (size_t)bh * Nq * D;
-    const uint16_t *Kg = static_cast<const uint16_t *>(p.k) + (size_t)bh * Nk * D;
-    const uint16_t *Vg = static_cast<const uint16_t *>(p.v) + (size_t)bh * Nk * D;
-    const uint8_t *Mg = p.mask ? p.mask + (size_t)b * Nk : nullptr;
-
-    // Q fragments: B operand of S^T = K . Q^T.  k-step kk covers head dims
-    // 16*kk .. 16*kk+15; this lane supplies dims 16*kk + 8*h .. +7 of its row.
     bf16x8 qf[D / 16];
+    int offk[D / 16];
+    int offv[D / 32];
+
+    float m_raw, mc, l_part;
+    f32x16 o[D / 32];
+    uint64_t kv_lo, kv_hi;
+    int mnext0, mnext1;
+
+    __device__ __forceinline__ void init(const Params &p, lds_char *lds_base)
     {
+        lds = lds_base;
+        const int tid = threadIdx.x;
+        lane = tid & 63;
+        w = tid >> 6;
+        l31 = lane & 31;
+        h = lane >> 5;
+
+        const int L = logical_tile(blockIdx.x, gridDim.x);
+        bh = L / p.n_qt;
+        const int qt = CAUSAL ? (p.n_qt - 1 - L % p.n_qt) : (L % p.n_qt);
+        b = bh / p.H;
+        q0 = qt * C::BM;
+        qw0 = q0 + 32 * w;          // first query row of this wave
+        qrow = qw0 + l31;           // this lane's query row
+        Nq = p.Nq;
+        Nk = p.Nk;
+        c = p.c;
+        reverse = p.reverse != 0;
+
+        const uint16_t *Qg = static_cast<const uint16_t *>(p.q) + (size_t)bh * Nq * D;
+        Kg = static_cast<const uint16_t *>(p.k) + (size_t)bh * Nk * D;
+        Vg = static_cast<const uint16_t *>(p.v) + (size_t)bh * Nk * D;
+        Mg = p.mask ? p.mask + (size_t)b * Nk : nullptr;
+
+        // Q fragments: B operand of S^T = K . Q^T.  k-step kk covers head
+        // dims 16*kk .. +15; this lane supplies dims 16*kk + 8*h .. +7.
         const int qr = qrow < Nq ? qrow : Nq - 1;
         const uint16_t *src = Qg + (size_t)qr * D + 8 * h;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
             qf[kk] = *reinterpret_cast<const bf16x8 *>(src + 16 * kk);
+
+        // Number of key tiles this workgroup needs.
+        n_t = (Nk + BN - 1) / BN;
+        if (CAUSAL) {
+            const int last_q = (q0 + C::BM < Nq ? q0 + C::BM : Nq) - 1;
+            const int need = last_q / BN + 1;
+            n_t = need < n_t ? need : n_t;
+        }
+
+        // Per-lane LDS byte offsets of the MFMA operands inside a stage.
+        //   K (A operand of S^T = K.Q^T, 16 bytes): key row 32*kb + l31,
+        //   dims 16*kk + 8*h .. +7, i.e. 16-byte chunk 2*kk + h of the row.
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            offk[kk] = l31 * C::ROW + 16 * ((2 * kk + h) ^ swz_k<D>(l31));
+        //   V (A operand of O^T += V^T.P^T) through the transposing read:
+        //   within a group of 16 lanes, lane i receives element i%4 of the
+        //   8-byte chunks addressed by lanes 4j + i/4 (j = 0..3).  Lane
+        //   i + 16g therefore addresses key row 16*t + 4*h + i/4 (+8 for the
+        //   second read), dims 32*db + 16*(g&1) + 4*(i&3) .. +3, and receives
+        //   V[16t + 4h + j][32db + l31] for j = 0..3: exactly the k-slots the
+        //   score layout gives P.
+        const int g = lane >> 4, i = lane & 15;
+        const int vrow = 4 * h + (i >> 2);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const int e = 8 * db + 4 * (g & 1) + (i & 3);   // 8-byte chunk of the row
+            offv[db] = vrow * C::ROW + 16 * ((e >> 1) ^ swz_v<D>(vrow)) + 8 * (e & 1);
+        }
+
+        m_raw = kNegInf;
+        mc = kNegInf;
+        l_part = 0.0f;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+        kv_lo = ~0ull;
+        kv_hi = ~0ull;
+        mnext0 = 0;
+        mnext1 = 0;
     }
 
-    // Number of key tiles this workgroup needs.
-    int n_t = (Nk + BN - 1) / BN;
-    if (CAUSAL) {
-        const int last_q = (q0 + C::BM < Nq ? q0 + C::BM : Nq) - 1;
-        const int need = last_q / BN + 1;
-        n_t = need < n_t ? need : n_t;
-    }
-
-    // Staging registers for the next tile.
-    u32x4 kreg[C::K_PER_T];
-    u32x4 vreg[C::V_PER_T][4];
-
-    auto load_tile = [&](int t) {
+    // LDS DMA of key tile t into stage st: wave w issues instructions w,
+    // w + NW, ...; instruction j covers rows j*ROWS_PER_DMA .. +ROWS_PER_DMA-1
+    // of both K and V.  Rows past N_k are clamped to the last key (their
+    // scores are masked).
+    __device__ __forceinline__ void issue_tile(int t, int st)
+    {
         const int k0 = t * BN;
 #pragma unroll
-        for (int i = 0; i < C::K_PER_T; ++i) {
-            const int ch = tid + i * C::T;
-            if (C::K_CHUNKS % C::T == 0 || ch < C::K_CHUNKS) {
-                const int row = ch / (D / 8), col = ch % (D / 8);
+        for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+            const int j = w + i * NW;
+            if (C::DMA_PER_TILE % NW == 0 || j < C::DMA_PER_TILE) {
+                const int row = j * C::ROWS_PER_DMA + lane / C::CH;
+                const int pc = lane % C::CH;
+                const int sk = pc ^ swz_k<D>(row);
+                const int sv = pc ^ swz_v<D>(row);
                 int kr = k0 + row;
                 kr = kr < Nk ? kr : Nk - 1;
-                kreg[i] = *reinterpret_cast<const u32x4 *>(Kg + (size_t)kr * D + 8 * col);
+                lds_char *dst = lds + st * C::STAGE + j * 1024;
+                __builtin_amdgcn_global_load_lds(Kg + (size_t)kr * D + 8 * sk,
+                                                 (__attribute__((address_space(3))) void *)dst,
+                                                 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(
+                    Vg + (size_t)kr * D + 8 * sv,
+                    (__attribute__((address_space(3))) void *)(dst + C::TILE), 16, 0, 0);
             }
         }
-#pragma unroll
-        for (int i = 0; i < C::V_PER_T; ++i) {
-            const int ch = tid + i * C::T;
-            if (C::V_CHUNKS % C::T == 0 || ch < C::V_CHUNKS) {
-                const int kq = ch % (BN / 4), c8 = ch / (BN / 4);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    int kr = k0 + 4 * kq + j;
-                    kr = kr < Nk ? kr : Nk - 1;
-                    vreg[i][j] = *reinterpret_cast<const u32x4 *>(Vg + (size_t)kr * D + 8 * c8);
-                }
-            }
-        }
-    };
-
-    auto store_tile = [&](int buf) {
-        uint16_t *Kl = lds + buf * C::BUF_ELEMS;
-        uint16_t *Vl = Kl + C::K_ELEMS;
-#pragma unroll
-        for (int i = 0; i < C::K_PER_T; ++i) {
-            const int ch = tid + i * C::T;
-            if (C::K_CHUNKS % C::T == 0 || ch < C::K_CHUNKS) {
-                const int row = ch / (D / 8), col = ch % (D / 8);
-                *reinterpret_cast<u32x4 *>(Kl + row * C::KP + 8 * col) = kreg[i];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < C::V_PER_T; ++i) {
-            const int ch = tid + i * C::T;
-            if (C::V_CHUNKS % C::T == 0 || ch < C::V_CHUNKS) {
-                const int kq = ch % (BN / 4), c8 = ch / (BN / 4);
-                // column j of the 8 loaded columns -> V^T row 8*c8 + j, keys
-                // 4*kq .. 4*kq+3 (four bf16 = 8 bytes)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int wd = j >> 1, sh = (j & 1) * 16;
-                    const uint32_t e0 = (vreg[i][0][wd] >> sh) & 0xffffu;
-                    const uint32_t e1 = (vreg[i][1][wd] >> sh) & 0xffffu;
-                    const uint32_t e2 = (vreg[i][2][wd] >> sh) & 0xffffu;
-                    const uint32_t e3 = (vreg[i][3][wd] >> sh) & 0xffffu;
-                    u32x2 pk;
-                    pk[0] = e0 | (e1 << 16);
-                    pk[1] = e2 | (e3 << 16);
-                    *reinterpret_cast<u32x2 *>(Vl + (8 * c8 + j) * C::VP + 4 * kq) = pk;
-                }
-            }
-        }
-    };
-
-    // Running state.  The lane pair (l, l ^ 32) shares one query row and the
-    // same m; each lane keeps its own partial l over the keys it holds.
-    float m_raw = kNegInf, mc = kNegInf, l_part = 0.0f;
-    f32x16 o[D / 32];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-
-    const float c = p.c;
-
-    if (n_t > 0) {
-        load_tile(p.reverse ? n_t - 1 : 0);
-        store_tile(0);
     }
-    __syncthreads();
 
-    for (int it = 0; it < n_t; ++it) {
-        const int t = p.reverse ? (n_t - 1 - it) : it;
-        const int buf = it & 1;
+    // One key-padding byte per lane for tile t (two for 128-key tiles),
+    // loaded a tile ahead and turned into bits after the next wait.
+    __device__ __forceinline__ void load_mask(int t)
+    {
+        const int j0 = t * BN + lane;
+        mnext0 = (lane < BN && j0 < Nk) ? Mg[j0] : 0;
+        mnext1 = (BN > 64 && lane + 64 < BN && j0 + 64 < Nk) ? Mg[j0 + 64] : 0;
+    }
+
+    __device__ __forceinline__ void take_mask()
+    {
+        kv_lo = __ballot(mnext0 != 0);
+        kv_hi = __ballot(mnext1 != 0);
+    }
+
+    // One iteration: prefetch tile it+1 into the other stage, compute tile it
+    // from stage ST, then wait for the prefetch and synchronise.
+    template <int ST>
+    __device__ __forceinline__ void iteration(int it)
+    {
+        const int t = reverse ? (n_t - 1 - it) : it;
         const bool has_next = it + 1 < n_t;
-        if (has_next) load_tile(p.reverse ? (n_t - 2 - it) : (it + 1));
+        if (has_next) {
+            const int tn = reverse ? (n_t - 2 - it) : (it + 1);
+            if (Mg) load_mask(tn);
+            issue_tile(tn, ST ^ 1);
+        }
 
         const int k0 = t * BN;
-        // Key-padding bits of this tile (bit i <=> key k0 + i visible).
-        uint64_t kv_lo = ~0ull, kv_hi = ~0ull;
-        if (Mg) {
-            const int j0 = k0 + lane;
-            const bool v0 = lane < BN && j0 < Nk && Mg[j0] != 0;
-            kv_lo = __ballot(v0);
-            if (BN > 64) {
-                const int j1 = j0 + 64;
-                const bool v1 = lane + 64 < BN && j1 < Nk && Mg[j1] != 0;
-                kv_hi = __ballot(v1);
-            }
-        }
         const bool tile_empty = Mg && kv_lo == 0 && (BN <= 64 || kv_hi == 0);
         // Keys beyond this wave's last row are all masked under causality.
         const bool wave_skip = tile_empty || (CAUSAL && k0 > qw0 + 31);
+        if (!wave_skip) compute<ST>(k0);
 
-        if (!wave_skip) {
-            const uint16_t *Kl = lds + buf * C::BUF_ELEMS;
-            const uint16_t *Vl = Kl + C::K_ELEMS;
-
-            // S^T = K . Q^T for the tile.
-            f32x16 s[C::NKB];
-#pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-#pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                        Kl + (32 * kb + l31) * C::KP + 16 * kk + 8 * h);
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
-                }
-
-            // Masks go in before the tile maximum ("The math of
-            // FlashAttention", "Pitfalls in implementing the recurrence").
-            const bool kv_partial = Mg && !(kv_lo == ~0ull && (BN <= 64 || kv_hi == ~0ull));
-            const bool tail = k0 + C::BNA > Nk || BN < 32;
-            const bool diag = CAUSAL && (k0 + BN - 1 > qw0);
-            if (kv_partial || tail || diag) {
-                uint32_t vis[C::NKB];
-#pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb) {
-                    const int first = k0 + 32 * kb + 4 * h;  // key of kpos 0
-                    int lim = (BN < 32 ? k0 + BN : Nk) - first;
-                    if (BN < 32 && Nk - first < lim) lim = Nk - first;
-                    if (CAUSAL && qrow - first + 1 < lim) lim = qrow - first + 1;
-                    // keys are at kpos 0-3, 8-11, 16-19, 24-27 of the lane's
-                    // bit word; a key at kpos k is visible iff its offset from
-                    // `first`, k, is below lim.
-                    uint32_t bits = prefix_bits(lim);
-                    if (Mg) {
-                        const uint64_t word = (kb < 2) ? kv_lo : kv_hi;
-                        const uint32_t kvw = (uint32_t)(word >> (32 * (kb & 1) + 4 * h));
-                        bits &= kvw;
-                    }
-                    vis[kb] = bits;
-                }
-                apply_visibility<C::NKB>(s, vis);
-            }
-
-            const float alpha = online_step<C::NKB, false>(s, m_raw, mc, l_part, c);
-
-            // Rescale o~ only when some row of the wave changed its maximum
-            // ("Rescale if maximum changed").
-            if (__any(alpha != 1.0f)) {
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-            }
-
-            // o~ += P . V as O^T += V^T . P^T.  k-step t covers keys
-            // 16t .. 16t+15; this lane's 8 weights are registers 8*(t%2) ..
-            // 8*(t%2)+7 of key block t/2, i.e. keys 16t + 4h + {0..3, 8..11}.
-#pragma unroll
-            for (int t16 = 0; t16 < C::NT16; ++t16) {
-                bf16x8 pb;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) pb[i] = (__bf16)s[t16 >> 1][8 * (t16 & 1) + i];
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const uint16_t *row = Vl + (32 * db + l31) * C::VP + 16 * t16 + 4 * h;
-                    const u32x2 lo = *reinterpret_cast<const u32x2 *>(row);
-                    const u32x2 hi = *reinterpret_cast<const u32x2 *>(row + 8);
-                    u32x4 av;
-                    av[0] = lo[0]; av[1] = lo[1]; av[2] = hi[0]; av[3] = hi[1];
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, av), pb, o[db], 0, 0, 0);
-                }
-            }
-        }
-
-        if (has_next) store_tile(buf ^ 1);
+        wait_vmem();
         __syncthreads();
+        if (Mg && has_next) take_mask();
     }
 
-    // Epilogue: o = o~ / l, lse = m + ln l; a row with no visible key gets
-    // o = 0 and lse = -inf.
-    const float l_row = l_part + __shfl_xor(l_part, 32);
-    const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
-    if (qrow < Nq) {
+    template <int ST>
+    __device__ __forceinline__ void compute(int k0)
+    {
+        lds_char *const sk = lds + ST * C::STAGE;
+        lds_char *const sv = sk + C::TILE;
+
+        // S^T = K . Q^T for the tile.
+        f32x16 s[C::NKB];
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb) {
+                const bf16x8 a = *(const lds_bf16x8 *)(sk + kb * 32 * C::ROW + offk[kk]);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
+            }
+
+        // Masks go in before the tile maximum ("The math of FlashAttention",
+        // "Pitfalls in implementing the recurrence").
+        const bool kv_partial = Mg && !(kv_lo == ~0ull && (BN <= 64 || kv_hi == ~0ull));
+        const bool tail = k0 + C::BNA > Nk || BN < 32;
+        const bool diag = CAUSAL && (k0 + BN - 1 > qw0);
+        if (kv_partial || tail || diag) {
+            uint32_t vis[C::NKB];
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb) {
+                const int first = k0 + 32 * kb + 4 * h;  // key of kpos 0
+                int lim = (BN < 32 ? k0 + BN : Nk) - first;
+                if (BN < 32 && Nk - first < lim) lim = Nk - first;
+                if (CAUSAL && qrow - first + 1 < lim) lim = qrow - first + 1;
+                // keys sit at kpos 0-3, 8-11, 16-19, 24-27 of the lane's bit
+                // word; the key at kpos k is visible iff k < lim.
+                uint32_t bits = prefix_bits(lim);
+                if (Mg) {
+                    const uint64_t word = (kb < 2) ? kv_lo : kv_hi;
+                    bits &= (uint32_t)(word >> (32 * (kb & 1) + 4 * h));
+                }
+                vis[kb] = bits;
+            }
+            apply_visibility<C::NKB>(s, vis);
+        }
+
+        const float alpha = online_step<C::NKB, false>(s, m_raw, mc, l_part, c);
+
+        // Rescale o~ only when some row of the wave changed its maximum
+        // ("Rescale if maximum changed").
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        }
+
+        // o~ += P . V as O^T += V^T . P^T.  k-step t16 covers keys 16*t16 ..
+        // +15; this lane's 8 weights are registers 8*(t16%2) .. +7 of key
+        // block t16/2, i.e. keys 16*t16 + 4h + {0..3, 8..11}.
+#pragma unroll
+        for (int t16 = 0; t16 < C::NT16; ++t16) {
+            bf16x8 pb;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pb[i] = (__bf16)s[t16 >> 1][8 * (t16 & 1) + i];
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                lds_char *row = sv + 16 * t16 * C::ROW + offv[db];
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)row);
+                const s16x4 hi =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(row + 8 * C::ROW));
+                const s16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                                pb, o[db], 0, 0, 0);
+            }
+        }
+    }
+
+    // o = o~ / l, lse = m + ln l; a row with no visible key gets o = 0 and
+    // lse = -inf.
+    __device__ __forceinline__ void epilogue(const Params &p)
+    {
+        const float l_row = l_part + __shfl_xor(l_part, 32);
+        const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
+        if (qrow >= Nq) return;
         uint16_t *Og = static_cast<uint16_t *>(p.o) + ((size_t)bh * Nq + qrow) * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -431,6 +479,29 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_bf16_kernel(const Params p)
             p.lse[(size_t)bh * Nq + qrow] =
                 l_row > 0.0f ? (mc + __builtin_amdgcn_logf(l_row)) * kLn2 : kNegInf;
     }
+};
+
+template <int D, int BN, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 2) void fa_fwd_bf16_kernel(const Params p)
+{
+    extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
+    Bf16Fwd<D, BN, NW, CAUSAL> k;
+    k.init(p, (lds_char *)lds_raw);
+
+    if (k.n_t > 0) {
+        const int t0 = k.reverse ? k.n_t - 1 : 0;
+        if (k.Mg) k.load_mask(t0);
+        k.issue_tile(t0, 0);
+    }
+    wait_vmem();
+    __syncthreads();
+    if (k.Mg) k.take_mask();
+
+    for (int it = 0; it < k.n_t; it += 2) {
+        k.template iteration<0>(it);
+        if (it + 1 < k.n_t) k.template iteration<1>(it + 1);
+    }
+    k.epilogue(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -655,23 +726,34 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_f32_kernel(const Params p)
 // Launchers
 // ---------------------------------------------------------------------------
 // Dynamic LDS above the default limit is opted into once per kernel and
-// device.
-template <auto Kernel>
-static hipError_t launch(int grid, int threads, size_t lds, hipStream_t stream, const Params &p)
+// device; `done` is the per-kernel record of devices already set up.
+static hipError_t launch(const void *kernel, void (*fn)(Params), std::atomic<uint64_t> &done,
+                         int grid, int threads, size_t lds, hipStream_t stream, const Params &p)
 {
-    static std::atomic<uint64_t> attr_done{0};
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     const uint64_t bit = 1ull << (dev & 63);
-    if (!(attr_done.load(std::memory_order_acquire) & bit)) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(Kernel),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (!(done.load(std::memory_order_acquire) & bit)) {
+        e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
-        attr_done.fetch_or(bit, std::memory_order_acq_rel);
+        done.fetch_or(bit, std::memory_order_acq_rel);
     }
-    hipLaunchKernelGGL(Kernel, dim3(grid), dim3(threads), lds, stream, p);
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(threads), lds, stream, p);
     return hipGetLastError();
+}
+
+template <int D, int BN, int NW, bool CAUSAL, bool BF16>
+static hipError_t launch_instance(int grid, int threads, size_t lds, hipStream_t stream,
+                                  const Params &p)
+{
+    static std::atomic<uint64_t> done{0};
+    void (*fn)(Params);
+    if constexpr (BF16)
+        fn = fa_fwd_bf16_kernel<D, BN, NW, CAUSAL>;
+    else
+        fn = fa_fwd_f32_kernel<D, BN, NW, CAUSAL>;
+    return launch(reinterpret_cast<const void *>(fn), fn, done, grid, threads, lds, stream, p);
 }
 
 template <int D, int BN>
@@ -683,8 +765,8 @@ static hipError_t dispatch_bf16(const Params &p0, int causal, int B, int H, hipS
     p.n_qt = (p.Nq + C::BM - 1) / C::BM;
     const int grid = B * H * p.n_qt;
     if (causal)
-        return launch<fa_fwd_bf16_kernel<D, BN, NW, true>>(grid, C::T, C::LDS_BYTES, stream, p);
-    return launch<fa_fwd_bf16_kernel<D, BN, NW, false>>(grid, C::T, C::LDS_BYTES, stream, p);
+        return launch_instance<D, BN, NW, true, true>(grid, C::T, C::LDS_BYTES, stream, p);
+    return launch_instance<D, BN, NW, false, true>(grid, C::T, C::LDS_BYTES, stream, p);
 }
 
 template <int D, int BN>
@@ -696,8 +778,8 @@ static hipError_t dispatch_f32(const Params &p0, int causal, int B, int H, hipSt
     p.n_qt = (p.Nq + C::BM - 1) / C::BM;
     const int grid = B * H * p.n_qt;
     if (causal)
-        return launch<fa_fwd_f32_kernel<D, BN, NW, true>>(grid, C::T, C::LDS_BYTES, stream, p);
-    return launch<fa_fwd_f32_kernel<D, BN, NW, false>>(grid, C::T, C::LDS_BYTES, stream, p);
+        return launch_instance<D, BN, NW, true, false>(grid, C::T, C::LDS_BYTES, stream, p);
+    return launch_instance<D, BN, NW, false, false>(grid, C::T, C::LDS_BYTES, stream, p);
 }
 
 template <int D>

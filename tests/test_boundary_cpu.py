@@ -116,3 +116,14 @@ def test_product_path_is_independent_of_the_oracle():
     out = subprocess.run(["objdump", "-p", fa.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     assert "faref" not in out
+
+
+def test_every_kernel_has_its_host_stub():
+    """A kernel whose host-side stub was not emitted shows up as an undefined
+    symbol and would only fail when the library is loaded on the GPU."""
+    out = subprocess.run(["nm", "-C", fa.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    undefined = [l for l in out.splitlines() if " U " in l and "fa::" in l]
+    assert not undefined, undefined
+    defined = [l for l in out.splitlines() if "fa::fa_fwd_" in l and "_kernel<" in l]
+    assert len(defined) >= 32, len(defined)
