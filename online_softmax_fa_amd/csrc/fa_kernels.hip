@@ -94,6 +94,24 @@ __device__ __forceinline__ void apply_visibility(f32x16 (&s)[NKB], const uint32_
             s[kb][r] = ((vis[kb] >> kpos(r)) & 1u) ? s[kb][r] : kNegInf;
 }
 
+// Value of x in the lane l ^ 32 combined with x by `op`, in every lane: one
+// v_permlane32_swap exchanges the two 32-lane halves, and both operands of
+// the combination are the same two values in every lane (so both halves get
+// bitwise the same result).
+__device__ __forceinline__ float pair_max(float x)
+{
+    const int xi = __builtin_bit_cast(int, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+    return fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x)
+{
+    const int xi = __builtin_bit_cast(int, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+    return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+}
+
 // One step of the recurrence on a tile of raw scores held in s (NKB blocks of
 // 16 per lane).  m_raw / mc: running max (raw score units) and fl(m_raw * c),
 // both -inf while no visible key has been seen; l_part: this lane's share of
@@ -118,7 +136,7 @@ __device__ __forceinline__ float online_step(f32x16 (&s)[NKB], float &m_raw, flo
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = pair_max(mx);
 
     const float m_new = fmaxf(m_raw, mx);
     const bool empty = (m_new == kNegInf);
@@ -226,6 +244,8 @@ struct Bf16Fwd {
     bf16x8 qf[D / 16];
     int offk[D / 16];
     int offv[D / 32];
+    int dmak[C::DMA_PER_WAVE];     // per-lane element offsets of the DMA sources
+    int dmav[C::DMA_PER_WAVE];     // within a tile (row-major K / V rows)
 
     float m_raw, mc, l_part;
     f32x16 o[D / 32];
@@ -237,7 +257,9 @@ struct Bf16Fwd {
         lds = lds_base;
         const int tid = threadIdx.x;
         lane = tid & 63;
-        w = tid >> 6;
+        // the wave index is uniform across the wave; reading it from lane 0
+        // lets the compiler keep every per-wave decision in scalar registers
+        w = __builtin_amdgcn_readfirstlane(tid >> 6);
         l31 = lane & 31;
         h = lane >> 5;
 
@@ -295,6 +317,18 @@ struct Bf16Fwd {
             offv[db] = vrow * C::ROW + 16 * ((e >> 1) ^ swz_v<D>(vrow)) + 8 * (e & 1);
         }
 
+        // DMA instruction i of this wave covers rows (w + i*NW)*ROWS_PER_DMA
+        // .. +ROWS_PER_DMA-1 of a tile; the lane fills 16-byte slot
+        // lane % CH of row lane / CH and fetches the global chunk that the
+        // row's swizzle places there.
+#pragma unroll
+        for (int i2 = 0; i2 < C::DMA_PER_WAVE; ++i2) {
+            const int row = (w + i2 * NW) * C::ROWS_PER_DMA + lane / C::CH;
+            const int pc = lane % C::CH;
+            dmak[i2] = row * D + 8 * (pc ^ swz_k<D>(row));
+            dmav[i2] = row * D + 8 * (pc ^ swz_v<D>(row));
+        }
+
         m_raw = kNegInf;
         mc = kNegInf;
         l_part = 0.0f;
@@ -315,23 +349,29 @@ struct Bf16Fwd {
     __device__ __forceinline__ void issue_tile(int t, int st)
     {
         const int k0 = t * BN;
+        const uint16_t *kt = Kg + (size_t)k0 * D;     // wave-uniform tile bases
+        const uint16_t *vt = Vg + (size_t)k0 * D;
+        const bool full = k0 + BN <= Nk;
 #pragma unroll
         for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
             const int j = w + i * NW;
             if (C::DMA_PER_TILE % NW == 0 || j < C::DMA_PER_TILE) {
-                const int row = j * C::ROWS_PER_DMA + lane / C::CH;
-                const int pc = lane % C::CH;
-                const int sk = pc ^ swz_k<D>(row);
-                const int sv = pc ^ swz_v<D>(row);
-                int kr = k0 + row;
-                kr = kr < Nk ? kr : Nk - 1;
+                int ok = dmak[i], ov = dmav[i];
+                if (!full) {
+                    // rows past N_k re-read the last key (their scores are masked)
+                    const int row = j * C::ROWS_PER_DMA + lane / C::CH;
+                    const int over = k0 + row - (Nk - 1);
+                    if (over > 0) {
+                        ok -= over * D;
+                        ov -= over * D;
+                    }
+                }
                 lds_char *dst = lds + st * C::STAGE + j * 1024;
-                __builtin_amdgcn_global_load_lds(Kg + (size_t)kr * D + 8 * sk,
+                __builtin_amdgcn_global_load_lds(kt + ok,
                                                  (__attribute__((address_space(3))) void *)dst,
                                                  16, 0, 0);
                 __builtin_amdgcn_global_load_lds(
-                    Vg + (size_t)kr * D + 8 * sv,
-                    (__attribute__((address_space(3))) void *)(dst + C::TILE), 16, 0, 0);
+                    vt + ov, (__attribute__((address_space(3))) void *)(dst + C::TILE), 16, 0, 0);
             }
         }
     }
@@ -456,7 +496,7 @@ struct Bf16Fwd {
     // lse = -inf.
     __device__ __forceinline__ void epilogue(const Params &p)
     {
-        const float l_row = l_part + __shfl_xor(l_part, 32);
+        const float l_row = pair_sum(l_part);
         const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
         if (qrow >= Nq) return;
         uint16_t *Og = static_cast<uint16_t *>(p.o) + ((size_t)bh * Nq + qrow) * D;
@@ -481,8 +521,16 @@ struct Bf16Fwd {
     }
 };
 
+// Two workgroups per CU when their LDS fits (then at most 256 VGPRs per
+// lane); one otherwise.
+constexpr int bf16_blocks_per_cu(int d, int bn)
+{
+    return 2 * 2 * (bn < 32 ? 32 : bn) * d * 2 <= 81920 ? 2 : 1;
+}
+
 template <int D, int BN, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 2) void fa_fwd_bf16_kernel(const Params p)
+__global__ __launch_bounds__(NW * 64, bf16_blocks_per_cu(D, BN)) void fa_fwd_bf16_kernel(
+    const Params p)
 {
     extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
     Bf16Fwd<D, BN, NW, CAUSAL> k;
@@ -702,7 +750,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_f32_kernel(const Params p)
             }
     }
 
-    const float l_row = l_part + __shfl_xor(l_part, 32);
+    const float l_row = pair_sum(l_part);
     const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
     if (qrow < Nq) {
         float *Og = static_cast<float *>(p.o) + ((size_t)bh * Nq + qrow) * D;
