@@ -12,6 +12,9 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--block-n BN] [--no-cpu-baseline] [--cpu-seconds S]
+       python bench.py --copy-calibration MIB
+           runs only a plain device-to-device copy of MIB MiB (3 launches), the
+           reference against which hardware byte counters are scaled
 """
 
 import argparse
@@ -110,6 +113,7 @@ def main():
     ap.add_argument("--block-n", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -122,6 +126,15 @@ def main():
     from online_softmax_fa_amd import inputs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return
     fa.load_library()
     dev = torch.device("cuda:0")
     w = inputs.workload(args.workload)

@@ -113,23 +113,25 @@ __device__ __forceinline__ float pair_sum(float x)
 }
 
 // One step of the recurrence on a tile of raw scores held in s (NKB blocks of
-// 16 per lane).  m_raw / mc: running max (raw score units) and fl(m_raw * c),
-// both -inf while no visible key has been seen; l_part: this lane's share of
-// the running denominator.  Turns s into the weights p and returns alpha.
+// 16 per lane), as the fp32 kernel runs it.  m_raw: running max in raw score
+// units (-inf while no visible key has been seen); l_part: this lane's share
+// of the running denominator.  Turns s into the weights p and returns alpha.
 // c = scale * log2(e) > 0, so the max of raw scores is the max of scaled ones.
 //
 // "2.2b: FlashAttention -- Online Softmax", "The Complete Online Softmax
 // Algorithm": m_block, m_new = max(m, m_block), scale = exp(m - m_new),
-// P = exp(S - m_new), l = l*scale + sum(P).
+// P = exp(S - m_new), l = l*scale + sum(P).  Weights are measured against m
+// itself, (s - m)*c, so the row maximum maps to exp2(0) = 1 exactly, and
+// alpha = exp2((m_old - m_new)*c), whose difference is exact.
 // While every key seen so far is masked, m_new is -inf and exp(m - m_new)
 // would be exp(-inf + inf).  The pages never meet this case; the reading here
 // is that such a tile changes nothing: alpha = 1 on the empty state and every
 // weight is exp2(-inf) = 0 (the exponent base is taken as 0 for the weights).
 // The first tile with a visible key then gets alpha = exp2(-inf) = 0, as the
 // pages' -inf initialisation intends.
-template <int NKB, bool ACCURATE>
-__device__ __forceinline__ float online_step(f32x16 (&s)[NKB], float &m_raw, float &mc,
-                                             float &l_part, float c)
+template <int NKB>
+__device__ __forceinline__ float online_step(f32x16 (&s)[NKB], float &m_raw, float &l_part,
+                                             float c)
 {
     float mx = kNegInf;
 #pragma unroll
@@ -141,32 +143,80 @@ __device__ __forceinline__ float online_step(f32x16 (&s)[NKB], float &m_raw, flo
     const float m_new = fmaxf(m_raw, mx);
     const bool empty = (m_new == kNegInf);
     const float base = empty ? 0.0f : m_new;
-    const float mc_new = base * c;
-    // The exponent of alpha must use the same reference as the weights: the
-    // fast path measures every weight against the rounded fl(m*c), so alpha is
-    // exp2(fl(m_old*c) - fl(m_new*c)); the accurate path measures them against
-    // m itself, so alpha is exp2((m_old - m_new)*c), whose difference is exact.
-    const float alpha = empty      ? 1.0f
-                        : ACCURATE ? __builtin_amdgcn_exp2f((m_raw - m_new) * c)
-                                   : __builtin_amdgcn_exp2f(mc - mc_new);
+    const float alpha = empty ? 1.0f : __builtin_amdgcn_exp2f((m_raw - m_new) * c);
 
     float sum = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            // ACCURATE: (s - m) first, so the row maximum maps to exp2(0) = 1
-            // exactly; otherwise a single fma in the log2 domain.
-            const float e = ACCURATE ? (s[kb][r] - base) * c
-                                     : __builtin_fmaf(s[kb][r], c, -mc_new);
-            const float pv = __builtin_amdgcn_exp2f(e);
+            const float pv = __builtin_amdgcn_exp2f((s[kb][r] - base) * c);
             s[kb][r] = pv;
             sum += pv;
         }
     l_part = l_part * alpha + sum;
     m_raw = m_new;
-    mc = empty ? kNegInf : mc_new;
     return alpha;
+}
+
+// The recurrence step of the bf16 kernel, with a lagging reference.
+//
+// The exponent base mc = fl(m_ref * c) (log2 units) follows the running
+// maximum, but moves only when a tile's maximum exceeds it by more than
+// kLag.  Until then the weights exp2(s*c - mc) may exceed 1, up to
+// 2^kLag = 256 -- far from any fp32 or bf16 limit -- and alpha is exactly 1,
+// so the 64-multiply rescale of o~ is skipped; when the base does move,
+// alpha = exp2(mc_old - mc_new) < 2^-kLag rescales l and o~ as the pages'
+// recurrence does.  l and o~ are always stated against the same base, so
+// o~ / l and lse = (mc + log2 l) ln 2 are the same quantities as with the
+// exact running maximum ("2.2b", "Why This Algorithm is Exact": any common
+// reference cancels; "The math of FlashAttention", "Proof of numerical
+// stability": here every exponent is at most kLag instead of 0).
+//
+// s: raw scores in, weights out; pb: the weights as bf16 P.V operands (k-step
+// t16 = registers 8*(t16%2) .. +7 of key block t16/2); l_part: this lane's
+// share of l, summed over the fp32 weights.  Returns whether o~ must be
+// rescaled by `alpha`:
+// some row of the wave moved its base after having seen a visible key.
+// While every key so far is masked mc stays -inf and the weights are
+// exp2(-inf) = 0.
+static constexpr float kLag = 8.0f;
+
+template <int NKB, int NT16>
+__device__ __forceinline__ bool lazy_step(f32x16 (&s)[NKB], bf16x8 (&pb)[NT16], float &mc,
+                                          float &l_part, float c, float &alpha)
+{
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = pair_max(mx);
+    const float mxc = mx * c;                       // -inf when the tile is all masked
+    const bool grow = mxc > mc + kLag;              // always true on the first visible tile
+    const float mc_new = grow ? mxc : mc;
+    alpha = grow ? __builtin_amdgcn_exp2f(mc - mc_new) : 1.0f;
+    const bool rescale = __any(grow && mc != kNegInf);
+    mc = mc_new;
+    const float base = (mc_new == kNegInf) ? 0.0f : mc_new;
+
+    // l sums the fp32 weights (before they are rounded for the product), so
+    // lse keeps fp32 accuracy; four partial sums keep the adds independent.
+    float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -base));
+            s[kb][r] = pv;
+            sum[r & 3] += pv;
+        }
+#pragma unroll
+    for (int t16 = 0; t16 < NT16; ++t16)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb[t16][i] = (__bf16)s[t16 >> 1][8 * (t16 & 1) + i];
+    l_part = l_part * alpha + ((sum[0] + sum[1]) + (sum[2] + sum[3]));
+    return rescale;
 }
 
 // ---------------------------------------------------------------------------
@@ -247,7 +297,7 @@ struct Bf16Fwd {
     int dmak[C::DMA_PER_WAVE];     // per-lane element offsets of the DMA sources
     int dmav[C::DMA_PER_WAVE];     // within a tile (row-major K / V rows)
 
-    float m_raw, mc, l_part;
+    float mc, l_part;   // exponent base fl(m_ref * c) (log2 units), this lane's share of l
     f32x16 o[D / 32];
     uint64_t kv_lo, kv_hi;
     int mnext0, mnext1;
@@ -329,7 +379,6 @@ struct Bf16Fwd {
             dmav[i2] = row * D + 8 * (pc ^ swz_v<D>(row));
         }
 
-        m_raw = kNegInf;
         mc = kNegInf;
         l_part = 0.0f;
 #pragma unroll
@@ -460,11 +509,11 @@ struct Bf16Fwd {
             apply_visibility<C::NKB>(s, vis);
         }
 
-        const float alpha = online_step<C::NKB, false>(s, m_raw, mc, l_part, c);
-
-        // Rescale o~ only when some row of the wave changed its maximum
-        // ("Rescale if maximum changed").
-        if (__any(alpha != 1.0f)) {
+        // The recurrence step with a lagging reference (lazy_step): bf16
+        // weights for the P.V product, l summed over exactly those weights.
+        bf16x8 pb[C::NT16];
+        float alpha;
+        if (lazy_step<C::NKB, C::NT16>(s, pb, mc, l_part, c, alpha)) {
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -476,9 +525,6 @@ struct Bf16Fwd {
         // block t16/2, i.e. keys 16*t16 + 4h + {0..3, 8..11}.
 #pragma unroll
         for (int t16 = 0; t16 < C::NT16; ++t16) {
-            bf16x8 pb;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) pb[i] = (__bf16)s[t16 >> 1][8 * (t16 & 1) + i];
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
                 lds_char *row = sv + 16 * t16 * C::ROW + offv[db];
@@ -487,7 +533,7 @@ struct Bf16Fwd {
                     __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(row + 8 * C::ROW));
                 const s16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
-                                                                pb, o[db], 0, 0, 0);
+                                                                pb[t16], o[db], 0, 0, 0);
             }
         }
     }
@@ -724,7 +770,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_f32_kernel(const Params p)
             apply_visibility<C::NKB>(s, vis);
         }
 
-        const float alpha = online_step<C::NKB, true>(s, m_raw, mc, l_part, c);
+        const float alpha = online_step<C::NKB>(s, m_raw, l_part, c);
         if (__any(alpha != 1.0f)) {
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)

@@ -170,3 +170,32 @@ def adversarial_cases(N=1024, seed=1002):
     cases["causal"] = (None, True)
     cases["all_masked"] = (torch.zeros(1, N, dtype=torch.uint8), False)
     return cases
+
+
+def adversarial_ramps(seed=1022, N=1024, dtype="f32"):
+    """Exact scores whose row maximum keeps rising across the keys.
+
+    Same construction as ``adversarial`` (scale 1/8, s = t_j + n/8), with
+    integer offsets t_j that ramp with the key index:
+      head 0: t_j = j // 16 - 32      (+4 per 64 keys: moderate growth)
+      head 1: head 0 reversed         (the maximum comes first)
+      head 2: t_j = j // 4 - 128      (+16 per 64 keys: the maximum jumps
+                                       every tile)
+      head 3: t_j = j // 64 - 8       (+1 per 64 keys: slow drift)
+    """
+    d, H = 64, 4
+    g = _gen(seed)
+    q = torch.zeros(1, H, N, d)
+    k = torch.zeros(1, H, N, d)
+    q[..., 0] = 8.0
+    q[..., 1:] = torch.randint(-1, 2, (1, H, N, d - 1), generator=g).float()
+    k[..., 1:] = torch.randint(-1, 2, (1, H, N, d - 1), generator=g).float()
+    j = torch.arange(N)
+    k[0, 0, :, 0] = (j // 16 - 32).float()
+    k[0, 2, :, 0] = (j // 4 - 128).float()
+    k[0, 3, :, 0] = (j // 64 - 8).float()
+    v = torch.randn(1, H, N, d, generator=g)
+    k[0, 1] = torch.flip(k[0, 0], dims=[0])
+    v[0, 1] = torch.flip(v[0, 0], dims=[0])
+    dt = TORCH_DTYPE[dtype]
+    return q.to(dt), k.to(dt), v.to(dt)

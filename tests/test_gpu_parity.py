@@ -124,6 +124,22 @@ def test_adversarial(dtype, case):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rising_maxima(dtype, causal):
+    """Row maxima that keep rising across the keys: the running maximum moves
+    by small steps on most tiles (head 0), by large steps on every tile
+    (head 2), slowly (head 3), or never after the first tile (head 1)."""
+    q, k, v = inputs.adversarial_ramps(dtype=dtype)
+    say("rising maxima %s causal=%d" % (dtype, causal))
+    o_ref, lse_ref = run_oracle(q, k, v, inputs.ADV_SCALE, causal=causal)
+    for bn in BLOCKS:
+        for rev in (False, True):
+            o, lse = run_gpu(q, k, v, inputs.ADV_SCALE, causal=causal, block_n=bn,
+                             reverse_kv=rev)
+            compare(o, lse, o_ref, lse_ref, dtype, what="ramps bn%d rev%d" % (bn, rev))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_adversarial_random_scaled(dtype):
     """Gaussian Q, K scaled so |scores| reach about 80.  bf16 is held to the
     bf16 bar.  For fp32 the scores themselves carry fp32 rounding before any
