@@ -164,14 +164,15 @@ __device__ __forceinline__ float online_step(f32x16 (&s)[NKB], float &m_raw, flo
 // The exponent base mc = fl(m_ref * c) (log2 units) follows the running
 // maximum, but moves only when a tile's maximum exceeds it by more than
 // kLag.  Until then the weights exp2(s*c - mc) may exceed 1, up to
-// 2^kLag = 256 -- far from any fp32 or bf16 limit -- and alpha is exactly 1,
+// 2^kLag = 256 here and 2^16 on the kernel's fast path that skips this step
+// -- far from any fp32 or bf16 limit -- and alpha is exactly 1,
 // so the 64-multiply rescale of o~ is skipped; when the base does move,
 // alpha = exp2(mc_old - mc_new) < 2^-kLag rescales l and o~ as the pages'
 // recurrence does.  l and o~ are always stated against the same base, so
 // o~ / l and lse = (mc + log2 l) ln 2 are the same quantities as with the
 // exact running maximum ("2.2b", "Why This Algorithm is Exact": any common
 // reference cancels; "The math of FlashAttention", "Proof of numerical
-// stability": here every exponent is at most kLag instead of 0).
+// stability": here every exponent is at most 16 instead of 0).
 //
 // s: raw scores in, weights out; pb: the weights as bf16 P.V operands (k-step
 // t16 = registers 8*(t16%2) .. +7 of key block t16/2); l_part: this lane's
@@ -330,6 +331,7 @@ struct Bf16Fwd {
         Vg = static_cast<const uint16_t *>(p.v) + (size_t)bh * Nk * D;
         Mg = p.mask ? p.mask + (size_t)b * Nk : nullptr;
 
+        const uint32_t lbase = (uint32_t)(uintptr_t)lds;
         // Q fragments: B operand of S^T = K . Q^T.  k-step kk covers head
         // dims 16*kk .. +15; this lane supplies dims 16*kk + 8*h .. +7.
         const int qr = qrow < Nq ? qrow : Nq - 1;
@@ -346,12 +348,12 @@ struct Bf16Fwd {
             n_t = need < n_t ? need : n_t;
         }
 
-        // Per-lane LDS byte offsets of the MFMA operands inside a stage.
+        // Per-lane LDS byte addresses (stage 0) of the MFMA operands.
         //   K (A operand of S^T = K.Q^T, 16 bytes): key row 32*kb + l31,
         //   dims 16*kk + 8*h .. +7, i.e. 16-byte chunk 2*kk + h of the row.
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
-            offk[kk] = l31 * C::ROW + 16 * ((2 * kk + h) ^ swz_k<D>(l31));
+            offk[kk] = lbase + l31 * C::ROW + 16 * ((2 * kk + h) ^ swz_k<D>(l31));
         //   V (A operand of O^T += V^T.P^T) through the transposing read:
         //   within a group of 16 lanes, lane i receives element i%4 of the
         //   8-byte chunks addressed by lanes 4j + i/4 (j = 0..3).  Lane
@@ -364,7 +366,8 @@ struct Bf16Fwd {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
             const int e = 8 * db + 4 * (g & 1) + (i & 3);   // 8-byte chunk of the row
-            offv[db] = vrow * C::ROW + 16 * ((e >> 1) ^ swz_v<D>(vrow)) + 8 * (e & 1);
+            offv[db] = lbase + C::TILE + vrow * C::ROW + 16 * ((e >> 1) ^ swz_v<D>(vrow)) +
+                       8 * (e & 1);
         }
 
         // DMA instruction i of this wave covers rows (w + i*NW)*ROWS_PER_DMA
@@ -464,26 +467,44 @@ struct Bf16Fwd {
         if (Mg && has_next) take_mask();
     }
 
+    // Raw scores S^T = K . Q^T of the tile in stage ST ("The math of
+    // FlashAttention", the tiled score block).
     template <int ST>
-    __device__ __forceinline__ void compute(int k0)
+    __device__ __forceinline__ void qk(f32x16 (&s)[C::NKB]) const
     {
-        lds_char *const sk = lds + ST * C::STAGE;
-        lds_char *const sv = sk + C::TILE;
-
-        // S^T = K . Q^T for the tile.
-        f32x16 s[C::NKB];
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+        bf16x8 kfr[D / 16][C::NKB];
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb) {
-                const bf16x8 a = *(const lds_bf16x8 *)(sk + kb * 32 * C::ROW + offk[kk]);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
+            for (int kb = 0; kb < C::NKB; ++kb)
+                kfr[kk][kb] = *(const lds_bf16x8 *)(uintptr_t)(offk[kk] + ST * C::STAGE +
+                                                                kb * 32 * C::ROW);
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb)
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[kk][kb], qf[kk], s[kb], 0, 0, 0);
+        // Interleave the K-fragment reads with the products, PF reads ahead
+        // of their use: a bounded number of live fragments, and the LDS
+        // latency is hidden behind the matrix cores.
+        {
+            constexpr int NM = D / 16 * C::NKB, PF = NM / 2;
+            __builtin_amdgcn_sched_group_barrier(0x100, PF, 5);
+#pragma unroll
+            for (int i = 0; i < NM - PF; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 5);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 5);
             }
+            __builtin_amdgcn_sched_group_barrier(0x008, PF, 5);
+        }
+    }
 
+    __device__ __forceinline__ void mask_scores(int k0, f32x16 (&s)[C::NKB]) const
+    {
         // Masks go in before the tile maximum ("The math of FlashAttention",
         // "Pitfalls in implementing the recurrence").
         const bool kv_partial = Mg && !(kv_lo == ~0ull && (BN <= 64 || kv_hi == ~0ull));
@@ -508,12 +529,44 @@ struct Bf16Fwd {
             }
             apply_visibility<C::NKB>(s, vis);
         }
+    }
 
-        // The recurrence step with a lagging reference (lazy_step): bf16
-        // weights for the P.V product, l summed over exactly those weights.
+    template <int ST>
+    __device__ __forceinline__ void compute(int k0)
+    {
+        f32x16 s[C::NKB];
+        qk<ST>(s);
+        mask_scores(k0, s);
         bf16x8 pb[C::NT16];
+        // Fast path: the weights against the current base, without the tile
+        // maximum.  They are kept when every lane's sum of them is at most
+        // 2^16, which bounds each weight by 2^16 too; the base stays where it
+        // is and alpha is 1.  Otherwise (a score far above the base, or a row
+        // with no base yet, whose weights come out +inf or NaN and fail the
+        // test) the scores are formed again from the K tile, which is still
+        // in LDS, and the step with the maximum runs.
+        float fs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
+                fs[r & 3] += s[kb][r];
+            }
+        const float tot = (fs[0] + fs[1]) + (fs[2] + fs[3]);
+        const bool done = !__any(!(tot <= 65536.0f));
+        if (done) {
+#pragma unroll
+            for (int t16 = 0; t16 < C::NT16; ++t16)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pb[t16][i] = (__bf16)s[t16 >> 1][8 * (t16 & 1) + i];
+            l_part += tot;
+        } else {
+            qk<ST>(s);
+            mask_scores(k0, s);
+        }
         float alpha;
-        if (lazy_step<C::NKB, C::NT16>(s, pb, mc, l_part, c, alpha)) {
+        if (!done && lazy_step<C::NKB, C::NT16>(s, pb, mc, l_part, c, alpha)) {
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -527,10 +580,10 @@ struct Bf16Fwd {
         for (int t16 = 0; t16 < C::NT16; ++t16) {
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-                lds_char *row = sv + 16 * t16 * C::ROW + offv[db];
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)row);
-                const s16x4 hi =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(row + 8 * C::ROW));
+                const uint32_t row = offv[db] + ST * C::STAGE + 16 * t16 * C::ROW;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)row);
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4 *)(uintptr_t)(row + 8 * C::ROW));
                 const s16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
                                                                 pb[t16], o[db], 0, 0, 0);
@@ -567,15 +620,19 @@ struct Bf16Fwd {
     }
 };
 
-// Two workgroups per CU when their LDS fits (then at most 256 VGPRs per
-// lane); one otherwise.
-constexpr int bf16_blocks_per_cu(int d, int bn)
+// Workgroups per CU the kernel is compiled for: two waves per SIMD (at most
+// 256 VGPRs per lane) when the LDS of that many workgroups fits, else one
+// workgroup.
+constexpr int bf16_blocks_per_cu(int d, int bn, int nw)
 {
-    return 2 * 2 * (bn < 32 ? 32 : bn) * d * 2 <= 81920 ? 2 : 1;
+    const int by_waves = 8 / nw;
+    const int by_lds = 2 * 2 * (bn < 32 ? 32 : bn) * d * 2 <= 81920 ? 2 : 1;
+    const int b = by_waves < by_lds ? by_waves : by_lds;
+    return b < 1 ? 1 : b;
 }
 
 template <int D, int BN, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, bf16_blocks_per_cu(D, BN)) void fa_fwd_bf16_kernel(
+__global__ __launch_bounds__(NW * 64, bf16_blocks_per_cu(D, BN, NW)) void fa_fwd_bf16_kernel(
     const Params p)
 {
     extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
@@ -691,7 +748,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_f32_kernel(const Params p)
         }
     };
 
-    float m_raw = kNegInf, mc = kNegInf, l_part = 0.0f;
+    float m_raw = kNegInf, l_part = 0.0f;
     f32x16 o[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
