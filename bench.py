@@ -4,6 +4,10 @@ One step = one fa_fwd call over the whole workload (every query row of every
 head), with Q, K, V already resident in HBM.  The default workload is the
 headline one: B=2, H=32, N_q=N_k=8192, d=128, bf16, causal.
 
+The defaults (200 timed launches after 50 warm-up ones, about a quarter of a
+second of GPU time) let the clocks settle: twenty launches after five read
+about 7% slower on the same device.
+
 Prints ONE JSON line on stdout (everything else goes to stderr):
   value      attention TFLOP/s = 4*B*H*N_q*N_k*d / t, halved for causal
   roofline   the kernel against the bf16 dense MFMA peak (2.5 PFLOP/s)
@@ -107,8 +111,8 @@ def cpu_baseline(w, seconds):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--block-n", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
