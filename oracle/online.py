@@ -28,6 +28,15 @@ while m is still -inf, where exp(m - m_new) would be exp(-inf + inf); the
 reading used here is that such a block leaves the empty state unchanged
 (alpha = 0, p = 0), which is what skipping it would do.  A row that ends with
 l = 0 gets o = 0 and lse = -inf.
+
+partial_state() and merge_states() give the same state for a set of keys
+directly and combine the states of disjoint key sets: each state is rewritten
+to the common base max(m_i) by the rescaling identity and the rewritten sums
+add ("The math of FlashAttention", sections "The running state: a max, a
+denominator, and an output", "The rescaling identity, derived" and "Proof of
+exactness", where block size and traversal order never enter the result).  The
+pages apply the identity to one running state and one new block; applying it to
+two states is the reading used for key ranges processed apart.
 """
 
 import math
@@ -100,3 +109,60 @@ def online_attention_row(scores, values=None, block=2, order=None, visible=None)
         o = None if v is None else o_t / l
         lse = m + math.log(l)
     return {"o": o, "m": m, "l": l, "lse": lse, "trace": trace}
+
+
+def partial_state(scores, values=None, visible=None):
+    """The running state (m, l, o~) of one set of keys, from its definition.
+
+    m is the largest visible score, l = sum_j exp(s_j - m) and
+    o~ = sum_j exp(s_j - m) v_j over the visible keys ("The math of
+    FlashAttention", "The running state: a max, a denominator, and an
+    output").  With no visible key: m = -inf, l = 0, o~ = 0 (the state the
+    recurrence starts from).
+
+    Returns a dict with m, l and o_tilde (a dv-vector, or None without values).
+    """
+    s = np.asarray(scores, dtype=np.float64).reshape(-1)
+    n = s.shape[0]
+    vis = np.ones(n, dtype=bool) if visible is None else np.asarray(visible, dtype=bool)
+    v = None if values is None else np.asarray(values, dtype=np.float64)
+    if v is not None and v.ndim == 1:
+        v = v[:, None]                                  # scalar values
+    dv = None if v is None else v.shape[1]
+    if not vis.any():
+        return {"m": -math.inf, "l": 0.0, "o_tilde": None if v is None else np.zeros(dv)}
+    m = float(np.max(s[vis]))
+    w = np.where(vis, np.exp(np.where(vis, s - m, 0.0)), 0.0)
+    return {"m": m, "l": float(np.sum(w)), "o_tilde": None if v is None else w @ v}
+
+
+def merge_states(states):
+    """Combine the states of disjoint key sets into the state of their union.
+
+    states: a sequence of dicts with m, l and o_tilde (as partial_state
+    returns).  The common base is M = max_i m_i; state i is rewritten to it by
+    alpha_i = exp(m_i - M) <= 1, applied to both l_i and o~_i (the rescaling
+    identity), and the rewritten sums add because the key sets are disjoint.
+    States with no visible key (m = -inf) contribute nothing.  Returns a dict
+    with m, l, o_tilde, o = o~ / l and lse = M + ln l; when no state has a
+    visible key, o = 0 and lse = -inf.
+    """
+    states = list(states)
+    if not states:
+        raise ValueError("at least one state is needed")
+    has_v = states[0]["o_tilde"] is not None
+    dv = len(states[0]["o_tilde"]) if has_v else 0
+    big_m = max(st["m"] for st in states)
+    l = 0.0
+    o_t = np.zeros(dv) if has_v else None
+    if big_m != -math.inf:
+        for st in states:
+            alpha = _exp(st["m"] - big_m)
+            l += alpha * st["l"]
+            if has_v:
+                o_t = o_t + alpha * np.asarray(st["o_tilde"], dtype=np.float64)
+    if l == 0.0:
+        return {"m": big_m, "l": 0.0, "o_tilde": o_t, "o": np.zeros(dv) if has_v else None,
+                "lse": -math.inf}
+    return {"m": big_m, "l": l, "o_tilde": o_t, "o": o_t / l if has_v else None,
+            "lse": big_m + math.log(l)}

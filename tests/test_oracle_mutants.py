@@ -47,6 +47,13 @@ PY_MUTANTS = {
                              "o_t = (alpha * o_t + p @ v[lo:hi]) / l")],
     "mask_after_block_max": [("        s[~vis] = -math.inf\n", "")],
     "alpha_sign": [("alpha = _exp(m - m_new)", "alpha = _exp(m_new - m)")],
+    "merge_l_not_rescaled": [('l += alpha * st["l"]', 'l += st["l"]')],
+    "merge_o_not_rescaled": [('o_t = o_t + alpha * np.asarray(st["o_tilde"], dtype=np.float64)',
+                              'o_t = o_t + np.asarray(st["o_tilde"], dtype=np.float64)')],
+    "merge_base_is_min": [('big_m = max(st["m"] for st in states)',
+                           'big_m = min(st["m"] for st in states)')],
+    "merge_alpha_sign": [('alpha = _exp(st["m"] - big_m)', 'alpha = _exp(big_m - st["m"])')],
+    "partial_state_unshifted": [("np.exp(np.where(vis, s - m, 0.0))", "np.exp(np.where(vis, s, 0.0))")],
 }
 
 

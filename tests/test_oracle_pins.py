@@ -9,7 +9,9 @@ Each check compares the oracle with something other than itself:
   - brute force of the plain definition, without max subtraction, in 50-digit
     decimal arithmetic on tiny inputs;
   - the textbook special case computed by a library routine (torch fp64
-    softmax followed by a matrix product).
+    softmax followed by a matrix product);
+  - for the merge of partial states: the pages' two-block example, and the
+    three-pass oracle over the union of the key ranges.
 """
 
 import json
@@ -21,7 +23,7 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle.online import online_attention_row
+from oracle.online import merge_states, online_attention_row, partial_state
 
 # Mutation testing (tests/test_oracle_mutants.py) reruns this file against
 # copies of the oracle with a planted mistake; these variables point there.
@@ -36,6 +38,8 @@ if _MUTANT_ONLINE:
     _mod = importlib.util.module_from_spec(_spec)
     _spec.loader.exec_module(_mod)
     online_attention_row = _mod.online_attention_row
+    partial_state = _mod.partial_state
+    merge_states = _mod.merge_states
 
 GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_examples.json")))
 
@@ -396,3 +400,70 @@ def test_row_subset_matches_full():
     o_r, lse_r, _ = oracle.attn_fwd(q, k, v, 0.3, causal=True, rows=rows)
     assert np.array_equal(o_r, o.reshape(-1, 8)[rows])
     assert np.array_equal(lse_r, lse.reshape(-1)[rows])
+
+
+# ---------------------------------------------------------------------------
+# Partial states of key ranges and their merge
+# ---------------------------------------------------------------------------
+def test_merge_reproduces_the_pages_two_block_example():
+    """The two blocks of the pages' worked example, each summarised on its own
+    and then merged, give the printed state after block 1 and the printed
+    final l, o~ and o, in either order ("The math of FlashAttention", "A
+    fully worked numeric example")."""
+    c = _case("attention_rows", "scalar_values_worked")
+    s, v = np.array(c["scores"], float), np.array(c["values"], float)
+    a = partial_state(s[:2], v[:2])
+    b = partial_state(s[2:], v[2:])
+    first = c["after"][0]
+    assert a["m"] == first["m"]
+    assert abs(a["l"] - first["l"]) <= c["l_trace_tol"]
+    assert abs(a["o_tilde"][0] - first["o_tilde"][0]) <= c["o_tilde_tol"]
+    for parts in ([a, b], [b, a]):
+        r = merge_states(parts)
+        assert r["m"] == c["after"][1]["m"]
+        assert abs(r["l"] - c["l"]) <= c["l_tol"]
+        assert abs(r["o_tilde"][0] - c["o_tilde_final"]) <= c["o_tilde_final_tol"]
+        assert abs(r["o"][0] - c["o"][0]) <= c["o_tol"]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_merge_of_key_ranges_matches_the_three_pass_oracle(seed):
+    """Splitting the keys of a row into consecutive ranges (some empty, some
+    fully masked), summarising each and merging gives the three-pass result
+    over all keys, for any order of the parts."""
+    rng = np.random.default_rng(300 + seed)
+    n, dv = int(rng.integers(5, 200)), 4
+    s = rng.standard_normal(n) * (5 + 20 * seed)
+    s[rng.integers(0, n)] += 60.0                        # one spike somewhere
+    v = rng.standard_normal((n, dv)).astype(np.float32)
+    vis = rng.random(n) > 0.3
+    vis[: n // 5] = False                                # a fully masked leading range
+    o_ref, lse_ref = oracle.attn_from_scores(s, v, vis)
+    cuts = sorted(set([0, n] + list(rng.integers(0, n + 1, size=int(rng.integers(0, 6))))))
+    cuts = [0, 0] + cuts[1:] if seed % 2 else cuts     # an empty range too
+    parts = [partial_state(s[a:b], v[a:b], vis[a:b]) for a, b in zip(cuts, cuts[1:])]
+    for order in (parts, parts[::-1], [parts[i] for i in rng.permutation(len(parts))]):
+        r = merge_states(order)
+        assert np.max(np.abs(r["o"] - o_ref)) < 1e-12
+        assert abs(r["lse"] - lse_ref) < 1e-12
+
+
+def test_merge_of_empty_and_distant_states():
+    """A state with no visible key changes nothing; if no state has one the
+    row is fully masked (o = 0, lse = -inf); states whose maxima are 2000
+    apart merge without overflow, the lower one contributing exp(-2000) = 0."""
+    v = np.array([[1.0, 2.0], [3.0, -1.0]])
+    full = partial_state([0.5, 1.5], v)
+    empty = partial_state([0.5, 1.5], v, [False, False])
+    assert empty["m"] == -math.inf and empty["l"] == 0.0 and np.all(empty["o_tilde"] == 0)
+    o_ref, lse_ref = oracle.attn_from_scores(np.array([0.5, 1.5]), v.astype(np.float32))
+    for parts in ([full, empty], [empty, full], [empty, full, empty]):
+        r = merge_states(parts)
+        assert np.max(np.abs(r["o"] - o_ref)) < 1e-14 and abs(r["lse"] - lse_ref) < 1e-14
+    r = merge_states([empty, empty])
+    assert np.all(r["o"] == 0) and r["lse"] == -math.inf
+    far = partial_state([2000.0, 1999.0], v)
+    r = merge_states([full, far])
+    o_far, lse_far = oracle.attn_from_scores(np.array([2000.0, 1999.0]), v.astype(np.float32))
+    assert np.all(np.isfinite(r["o"])) and np.max(np.abs(r["o"] - o_far)) < 1e-14
+    assert abs(r["lse"] - lse_far) < 1e-12
