@@ -46,6 +46,7 @@
 #ifndef FA_H
 #define FA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -62,7 +63,10 @@ typedef enum fa_status {
     FA_ERR_TILE = -6,      /* fa_opts.block_n is not 0, 16, 32, 64 or 128        */
     FA_ERR_DEVICE = -7,    /* the current HIP device is not a gfx950 GPU         */
     FA_ERR_LAUNCH = -8,    /* HIP reported an error when the kernel was enqueued */
-    FA_ERR_ALIAS = -9      /* o or lse overlaps an input buffer                  */
+    FA_ERR_ALIAS = -9,     /* an output overlaps an input or another output      */
+    FA_ERR_ARG = -10,      /* another argument is out of range: the traced row,
+                              num_splits, n_parts                                */
+    FA_ERR_WORKSPACE = -11 /* workspace NULL or smaller than required            */
 } fa_status;
 
 typedef enum fa_dtype {
@@ -110,24 +114,133 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
 /*
  * Test hooks.  A zeroed struct (or a NULL pointer) gives fa_fwd's behaviour.
  *
- *   block_n     keys per tile of the recurrence: 0 (library choice), 16, 32,
- *               64 or 128.  The result must not depend on it ("The math of
- *               FlashAttention", "Proof of exactness": block size never enters
- *               the result; the tiled-attention interview answer asks to vary
- *               the tile size when testing).
+ *   block_n     keys per tile of the recurrence: 0 (library choice, 64), 16,
+ *               32, 64 or 128.  The result must not depend on it ("The math
+ *               of FlashAttention", "Proof of exactness": block size never
+ *               enters the result; the tiled-attention interview answer asks
+ *               to vary the tile size when testing).
  *   reverse_kv  nonzero: visit the key tiles last to first.  The result must
  *               not depend on the order either ("The running state": blocks
  *               may be processed in any order).
+ *   trace       NULL, or a device array of ceil(N_k / block_n) * 4 floats
+ *               (block_n as used, 64 for 0) that receives the running state
+ *               of ONE query row after every key tile the kernel visits --
+ *               the per-block (m, l) printout the tiled-attention interview
+ *               answer recommends for debugging.  Entry i (the i-th tile
+ *               visited) is {tile index, m, l, 0}: l is the row's running
+ *               denominator stated against the reference m, given in raw
+ *               score units (q . k, before `scale`), so that after the tile
+ *               m * scale + ln(l) is the log of the sum of exp(scaled score)
+ *               over the keys absorbed so far (-inf and 0 while none is
+ *               visible).  For float32, m is the running maximum itself.  For
+ *               bfloat16, m lags it: the kernel moves its reference only when
+ *               a tile's scores exceed it by more than 16 / (scale * log2 e),
+ *               so running max - that bound <= m <= running max.  Tiles the
+ *               kernel never visits (above the causal diagonal of the row's
+ *               query tile) leave their entries untouched.
+ *   trace_b, trace_h, trace_row
+ *               the traced row: batch, head and query index, each in range
+ *               (else FA_ERR_ARG).  Ignored when trace is NULL.
  */
 typedef struct fa_opts {
     int block_n;
     int reverse_kv;
+    float *trace;
+    int trace_b;
+    int trace_h;
+    int trace_row;
 } fa_opts;
 
 int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
               int B, int H, int N_q, int N_k, int d, float scale, int causal,
               const uint8_t *kv_len_mask, int dtype, void *stream,
               const fa_opts *opts);
+
+/*
+ * Split-key forward pass and the merge of partial states.
+ *
+ * The keys of every query row are cut into num_splits consecutive ranges of
+ * whole key tiles (64 keys), processed by separate workgroups; each range
+ * yields the row's PARTIAL STATE over its keys, and a second kernel merges
+ * them.  A partial state is the pages' running state of a set of keys ("The
+ * math of FlashAttention", "The running state: a max, a denominator, and an
+ * output"), with its reference m given in raw score units:
+ *
+ *     m     a reference score (q . k, before `scale`), -inf if no key of the
+ *           range is visible; in practice the range's maximum or just below
+ *     l     sum_j exp(scale * (s_j - m))           over the range's visible keys
+ *     acc   sum_j exp(scale * (s_j - m)) * v_j     (d floats)
+ *
+ * Merging rewrites every state to the common reference M = max_i m_i by the
+ * rescaling identity (l_i and acc_i times exp(scale * (m_i - M)), "The
+ * rescaling identity, derived") and adds them: the key sets are disjoint and
+ * order does not matter ("Proof of exactness").  Then o = acc / l and
+ * lse = M * scale + ln l, with o = 0 and lse = -inf when every m_i is -inf.
+ * This is the step that serves few query rows over many keys (decoding), few
+ * heads, and -- across devices -- keys sharded over GPUs.
+ *
+ * Partial-state arrays are part-major: for part i and row r (of `rows`),
+ *     m[i * rows + r], l[i * rows + r], acc[(i * rows + r) * d + j].
+ */
+
+/*
+ * fa_splitkv_workspace_bytes -- device bytes fa_fwd_splitkv needs for these
+ * sizes: the partial states of num_splits parts of B*H*N_q rows, laid out as
+ * m (float[num_splits][rows]), l (same), then acc (float[num_splits][rows][d])
+ * starting at the next multiple of 256 bytes.  Returns 0 when an argument is
+ * out of range (see fa_fwd_splitkv).
+ */
+size_t fa_splitkv_workspace_bytes(int B, int H, int N_q, int d, int num_splits);
+
+/*
+ * fa_splitkv_splits -- the library's choice of num_splits for these sizes on
+ * the current device: enough workgroups to give every compute unit several,
+ * and at least 4 key tiles per range; 1 when the plain pass already fills the
+ * GPU.  Returns a value in [1, 256], or a negative fa_status.
+ */
+int fa_splitkv_splits(int B, int H, int N_q, int N_k, int d, int causal);
+
+/*
+ * fa_fwd_splitkv -- the same result as fa_fwd (all arguments as there,
+ * key tiles of 64), computed as num_splits partial states per row that are
+ * then merged.
+ *
+ *   num_splits       1 .. 256 (else FA_ERR_ARG).  Ranges may be empty when
+ *                    num_splits exceeds a row's tile count; they contribute
+ *                    nothing.
+ *   workspace        device memory of at least workspace_bytes =
+ *                    fa_splitkv_workspace_bytes(B, H, N_q, d, num_splits)
+ *                    bytes, 16-byte aligned, owned by the caller, overlapping
+ *                    no other argument (else FA_ERR_WORKSPACE / FA_ERR_ALIAS).
+ *                    Its contents on entry do not matter; on return (once the
+ *                    stream reaches that point) it holds the partial states in
+ *                    the layout above.  Two calls in flight must not share it.
+ *
+ * Two kernels are enqueued on `stream`; nothing is allocated or synchronised.
+ */
+int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+                   int B, int H, int N_q, int N_k, int d, float scale, int causal,
+                   const uint8_t *kv_len_mask, int dtype, int num_splits,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * fa_merge_states -- merge n_parts partial states per row (layout above) into
+ * o and lse.
+ *
+ *   m, l         device float[n_parts * rows]
+ *   acc          device float[n_parts * rows * d]
+ *   n_parts      >= 1 (else FA_ERR_ARG); rows >= 1 (else FA_ERR_SHAPE)
+ *   d            64 or 128
+ *   scale        the score multiplier the states were formed with (> 0)
+ *   o            device [rows, d] of `dtype` (bf16 rounded to nearest-even)
+ *   lse          device float[rows]
+ *
+ * A part whose m is -inf contributes nothing; its l and acc are not read.
+ * Otherwise l must be >= 0 and finite, as a real partial state's is.
+ */
+int fa_merge_states(const float *m, const float *l, const float *acc, int n_parts,
+                    int64_t rows, int d, float scale, void *o, float *lse, int dtype,
+                    void *stream);
 
 /*
  * fa_strerror -- a NUL-terminated description of a status code, never NULL.

@@ -9,10 +9,17 @@ raises.
 Entry points (same names and meaning as include/fa.h):
   fa_fwd(q, k, v, o, lse, B, H, N_q, N_k, d, scale, causal, kv_len_mask, dtype, stream)
   fa_fwd_ex(..., opts)
+  fa_splitkv_workspace_bytes(B, H, N_q, d, num_splits)
+  fa_splitkv_splits(B, H, N_q, N_k, d, causal)
+  fa_fwd_splitkv(..., dtype, num_splits, workspace, workspace_bytes, stream)
+  fa_merge_states(m, l, acc, n_parts, rows, d, scale, o, lse, dtype, stream)
   fa_strerror(code)
-and one convenience wrapper that allocates the outputs with torch:
-  attention(q, k, v, scale=None, causal=False, kv_len_mask=None, block_n=0, reverse_kv=False)
-      -> (o, lse)
+and convenience wrappers that allocate outputs (and workspace) with torch:
+  attention(q, k, v, scale=None, causal=False, kv_len_mask=None, block_n=0, reverse_kv=False,
+            out=None, trace=None)                                   -> (o, lse)
+  attention_splitkv(q, k, v, scale=None, causal=False, kv_len_mask=None, num_splits=None,
+                    out=None, workspace=None)                       -> (o, lse)
+  merge_states(m, l, acc, scale, out_dtype=None, out=None)          -> (o, lse)
 """
 
 import ctypes
@@ -31,6 +38,8 @@ FA_ERR_TILE = -6
 FA_ERR_DEVICE = -7
 FA_ERR_LAUNCH = -8
 FA_ERR_ALIAS = -9
+FA_ERR_ARG = -10
+FA_ERR_WORKSPACE = -11
 
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
@@ -43,7 +52,9 @@ class FaError(RuntimeError):
 
 
 class fa_opts(ctypes.Structure):
-    _fields_ = [("block_n", ctypes.c_int), ("reverse_kv", ctypes.c_int)]
+    _fields_ = [("block_n", ctypes.c_int), ("reverse_kv", ctypes.c_int),
+                ("trace", ctypes.c_void_p), ("trace_b", ctypes.c_int), ("trace_h", ctypes.c_int),
+                ("trace_row", ctypes.c_int)]
 
 
 _lib = None
@@ -67,6 +78,16 @@ def load_library(path=LIB_PATH):
     lib.fa_fwd_ex.argtypes = args + [ctypes.POINTER(fa_opts)]
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_strerror.argtypes = [ci]
+    sz, i64 = ctypes.c_size_t, ctypes.c_int64
+    lib.fa_splitkv_workspace_bytes.restype = sz
+    lib.fa_splitkv_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
+    lib.fa_splitkv_splits.restype = ci
+    lib.fa_splitkv_splits.argtypes = [ci, ci, ci, ci, ci, ci]
+    lib.fa_fwd_splitkv.restype = ci
+    lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, vp, ci, ci, vp,
+                                   sz, vp]
+    lib.fa_merge_states.restype = ci
+    lib.fa_merge_states.argtypes = [vp, vp, vp, ci, i64, ci, cf, vp, vp, ci, vp]
     _lib = lib
     return lib
 
@@ -107,22 +128,47 @@ def fa_fwd_ex(q, k, v, o, lse, B, H, N_q, N_k, d, scale, causal, kv_len_mask, dt
     _check(rc)
 
 
-def attention(q, k, v, scale=None, causal=False, kv_len_mask=None, block_n=0, reverse_kv=False,
-              out=None):
-    """o, lse for torch tensors q [B,H,Nq,d], k, v [B,H,Nk,d] on one GPU.
+def fa_splitkv_workspace_bytes(B, H, N_q, d, num_splits):
+    return int(load_library().fa_splitkv_workspace_bytes(B, H, N_q, d, num_splits))
 
-    q, k, v: contiguous float32 or bfloat16 CUDA (HIP) tensors; kv_len_mask:
-    None or a uint8 [B, Nk] CUDA tensor.  Outputs are allocated with torch
-    (o in the input dtype, lse float32) unless `out=(o, lse)` is given.  The
-    kernel runs on torch's current stream; nothing is synchronised.
-    """
+
+def fa_splitkv_splits(B, H, N_q, N_k, d, causal):
+    rc = load_library().fa_splitkv_splits(B, H, N_q, N_k, d, int(bool(causal)))
+    if rc < 0:
+        _check(rc)
+    return rc
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, B, H, N_q, N_k, d, scale, causal, kv_len_mask, dtype,
+                   num_splits, workspace, workspace_bytes, stream):
+    """C fa_fwd_splitkv."""
+    rc = load_library().fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N_q,
+                                       N_k, d, float(scale), int(bool(causal)), _ptr(kv_len_mask),
+                                       int(dtype), int(num_splits), _ptr(workspace),
+                                       int(workspace_bytes), stream)
+    _check(rc)
+
+
+def fa_merge_states(m, l, acc, n_parts, rows, d, scale, o, lse, dtype, stream):
+    """C fa_merge_states."""
+    rc = load_library().fa_merge_states(_ptr(m), _ptr(l), _ptr(acc), int(n_parts), int(rows),
+                                        int(d), float(scale), _ptr(o), _ptr(lse), int(dtype),
+                                        stream)
+    _check(rc)
+
+
+def _dtype_code(t):
     import torch
-    if q.dtype == torch.bfloat16:
-        dt = FA_DTYPE_BF16
-    elif q.dtype == torch.float32:
-        dt = FA_DTYPE_F32
-    else:
-        raise FaError(FA_ERR_DTYPE, "q must be float32 or bfloat16")
+    if t.dtype == torch.bfloat16:
+        return FA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return FA_DTYPE_F32
+    raise FaError(FA_ERR_DTYPE, "tensors must be float32 or bfloat16")
+
+
+def _check_qkv(q, k, v, kv_len_mask):
+    import torch
+    dt = _dtype_code(q)
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
             raise FaError(FA_ERR_SHAPE, "%s must be a contiguous 4-D GPU tensor of q's dtype" % name)
@@ -134,14 +180,90 @@ def attention(q, k, v, scale=None, causal=False, kv_len_mask=None, block_n=0, re
         if (kv_len_mask.dtype != torch.uint8 or not kv_len_mask.is_cuda
                 or not kv_len_mask.is_contiguous() or tuple(kv_len_mask.shape) != (B, Nk)):
             raise FaError(FA_ERR_SHAPE, "kv_len_mask must be a contiguous uint8 [B, N_k] GPU tensor")
+    return dt, B, H, Nq, Nk, d
+
+
+def _outputs(q, out):
+    import torch
+    if out is not None:
+        return out
+    B, H, Nq, _ = q.shape
+    return torch.empty_like(q), torch.empty(B, H, Nq, dtype=torch.float32, device=q.device)
+
+
+def attention_splitkv(q, k, v, scale=None, causal=False, kv_len_mask=None, num_splits=None,
+                      out=None, workspace=None):
+    """o, lse through fa_fwd_splitkv: the keys of every row cut into
+    num_splits ranges (None: the library's choice, fa_splitkv_splits), whose
+    partial states are merged.  The workspace (a uint8 CUDA tensor of at least
+    fa_splitkv_workspace_bytes) is allocated with torch unless given."""
+    import torch
+    dt, B, H, Nq, Nk, d = _check_qkv(q, k, v, kv_len_mask)
     if scale is None:
         scale = 1.0 / float(d) ** 0.5
+    if num_splits is None:
+        num_splits = fa_splitkv_splits(B, H, Nq, Nk, d, causal)
+    need = fa_splitkv_workspace_bytes(B, H, Nq, d, num_splits)
+    if need == 0:
+        raise FaError(FA_ERR_ARG, "num_splits must be in 1..256")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    o, lse = _outputs(q, out)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    fa_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_len_mask, dt, num_splits,
+                   workspace, workspace.numel() * workspace.element_size(), stream)
+    return o, lse
+
+
+def merge_states(m, l, acc, scale, out_dtype=None, out=None):
+    """o, lse from partial states m, l [n_parts, rows] and acc
+    [n_parts, rows, d] (contiguous float32 CUDA tensors, m in raw score units).
+    o has dtype out_dtype (float32 or bfloat16; default float32)."""
+    import torch
+    n_parts, rows, d = acc.shape
+    for name, t in (("m", m), ("l", l), ("acc", acc)):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise FaError(FA_ERR_SHAPE, "%s must be a contiguous float32 GPU tensor" % name)
+    if tuple(m.shape) != (n_parts, rows) or tuple(l.shape) != (n_parts, rows):
+        raise FaError(FA_ERR_SHAPE, "m and l must be [n_parts, rows] matching acc")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
     if out is None:
-        o = torch.empty_like(q)
-        lse = torch.empty(B, H, Nq, dtype=torch.float32, device=q.device)
+        o = torch.empty(rows, d, dtype=out_dtype, device=acc.device)
+        lse = torch.empty(rows, dtype=torch.float32, device=acc.device)
     else:
         o, lse = out
+    dt = _dtype_code(o)
+    stream = torch.cuda.current_stream(acc.device).cuda_stream
+    fa_merge_states(m, l, acc, n_parts, rows, d, scale, o, lse, dt, stream)
+    return o, lse
+
+
+def attention(q, k, v, scale=None, causal=False, kv_len_mask=None, block_n=0, reverse_kv=False,
+              out=None, trace=None):
+    """o, lse for torch tensors q [B,H,Nq,d], k, v [B,H,Nk,d] on one GPU.
+
+    q, k, v: contiguous float32 or bfloat16 CUDA (HIP) tensors; kv_len_mask:
+    None or a uint8 [B, Nk] CUDA tensor.  Outputs are allocated with torch
+    (o in the input dtype, lse float32) unless `out=(o, lse)` is given.  The
+    kernel runs on torch's current stream; nothing is synchronised.
+    trace: None, or (buffer, b, h, row) with buffer a float32 CUDA tensor of
+    ceil(N_k / block_n) * 4 elements: the per-tile state of that row
+    (fa_opts.trace in include/fa.h).
+    """
+    import torch
+    dt, B, H, Nq, Nk, d = _check_qkv(q, k, v, kv_len_mask)
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    o, lse = _outputs(q, out)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    opts = fa_opts(int(block_n), int(bool(reverse_kv)))
+    opts = fa_opts(int(block_n), int(bool(reverse_kv)), None, 0, 0, 0)
+    if trace is not None:
+        buf, tb, th, trow = trace
+        if buf.dtype != torch.float32 or not buf.is_cuda or not buf.is_contiguous():
+            raise FaError(FA_ERR_SHAPE, "the trace buffer must be a contiguous float32 GPU tensor")
+        bn = int(block_n) or 64
+        if buf.numel() < (Nk + bn - 1) // bn * 4:
+            raise FaError(FA_ERR_SHAPE, "the trace buffer needs ceil(N_k / block_n) * 4 floats")
+        opts.trace, opts.trace_b, opts.trace_h, opts.trace_row = buf.data_ptr(), tb, th, trow
     fa_fwd_ex(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_len_mask, dt, stream, opts)
     return o, lse

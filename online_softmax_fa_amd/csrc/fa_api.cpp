@@ -50,9 +50,16 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb)
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
-int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
-             int N_q, int N_k, int d, float scale, int causal, const uint8_t *kv_len_mask,
-             int dtype, void *stream, const fa_opts *opts)
+// Sizes of the buffers of one forward call, after validation.
+struct Sizes {
+    size_t qb, kb, lb, mb;   // bytes of q (and o), k (and v), lse, mask
+    int64_t rows;            // B * H * N_q
+};
+
+// Checks shared by the forward entry points, in the documented order.
+int check_fwd_args(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                   int H, int N_q, int N_k, int d, float scale, const uint8_t *kv_len_mask,
+                   int dtype, int n_split, Sizes &sz)
 {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
     if (B <= 0 || H <= 0 || N_q <= 0 || N_k <= 0) return FA_ERR_SHAPE;
@@ -60,34 +67,41 @@ int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, i
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
     if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_SCALE;
 
-    int block_n = opts ? opts->block_n : 0;
-    if (block_n != 0 && block_n != 16 && block_n != 32 && block_n != 64 && block_n != 128)
-        return FA_ERR_TILE;
-    if (block_n == 0) block_n = 64;
-
     // Index space: every element offset must fit in int64, and the grid
-    // (B*H*ceil(N_q/32) workgroups at most) in int32.
+    // (B*H*ceil(N_q/32)*n_split workgroups at most) in int32.
     const int64_t bh = (int64_t)B * H;
-    const int64_t nq_el = bh * N_q * d, nk_el = bh * N_k * d;
     if (bh > (int64_t)1 << 31 || (double)bh * N_q * d > 9.0e18 || (double)bh * N_k * d > 9.0e18)
         return FA_ERR_SHAPE;
-    if (bh * (((int64_t)N_q + 31) / 32) > INT32_MAX) return FA_ERR_SHAPE;
+    if ((double)bh * (((int64_t)N_q + 31) / 32) * n_split > (double)INT32_MAX) return FA_ERR_SHAPE;
 
     const size_t esz = dtype == FA_DTYPE_BF16 ? 2 : 4;
-    const size_t qb = (size_t)nq_el * esz, kb = (size_t)nk_el * esz;
-    const size_t lb = (size_t)bh * N_q * sizeof(float);
-    const size_t mb = kv_len_mask ? (size_t)B * N_k : 0;
+    sz.qb = (size_t)(bh * N_q * d) * esz;
+    sz.kb = (size_t)(bh * N_k * d) * esz;
+    sz.lb = (size_t)bh * N_q * sizeof(float);
+    sz.mb = kv_len_mask ? (size_t)B * N_k : 0;
+    sz.rows = bh * N_q;
     const void *ins[4] = {q, k, v, kv_len_mask};
-    const size_t in_bytes[4] = {qb, kb, kb, mb};
+    const size_t in_bytes[4] = {sz.qb, sz.kb, sz.kb, sz.mb};
     for (int i = 0; i < 4; ++i)
-        if (overlaps(o, qb, ins[i], in_bytes[i]) || overlaps(lse, lb, ins[i], in_bytes[i]))
+        if (overlaps(o, sz.qb, ins[i], in_bytes[i]) || overlaps(lse, sz.lb, ins[i], in_bytes[i]))
             return FA_ERR_ALIAS;
-    if (overlaps(o, qb, lse, lb)) return FA_ERR_ALIAS;
+    if (overlaps(o, sz.qb, lse, sz.lb)) return FA_ERR_ALIAS;
+    return FA_OK;
+}
 
-    int rc = check_device();
-    if (rc != FA_OK) return rc;
+// True if [p, p + n) overlaps any buffer of a forward call.
+bool overlaps_fwd(const void *p, size_t n, const void *q, const void *k, const void *v,
+                  const void *o, const float *lse, const uint8_t *mask, const Sizes &sz)
+{
+    return overlaps(p, n, q, sz.qb) || overlaps(p, n, k, sz.kb) || overlaps(p, n, v, sz.kb) ||
+           overlaps(p, n, o, sz.qb) || overlaps(p, n, lse, sz.lb) || overlaps(p, n, mask, sz.mb);
+}
 
+fa::Params make_params(const void *q, const void *k, const void *v, void *o, float *lse, int H,
+                       int N_q, int N_k, float scale, const uint8_t *kv_len_mask)
+{
     fa::Params p;
+    std::memset(&p, 0, sizeof p);
     p.q = q;
     p.k = k;
     p.v = v;
@@ -97,18 +111,70 @@ int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, i
     p.H = H;
     p.Nq = N_q;
     p.Nk = N_k;
-    p.n_qt = 0;
     p.c = (float)((double)scale * 1.4426950408889634073599);
     p.scale = scale;
-    p.reverse = (opts && opts->reverse_kv) ? 1 : 0;
+    p.n_split = 1;
+    return p;
+}
 
-    hipError_t e = fa::launch_fwd(p, dtype, d, block_n, causal ? 1 : 0, B, H,
-                                  static_cast<hipStream_t>(stream));
+int launch_status(hipError_t e)
+{
     if (e != hipSuccess) {
         g_last_hip = e;
         return FA_ERR_LAUNCH;
     }
     return FA_OK;
+}
+
+constexpr int kMaxSplits = 256;
+constexpr int kSplitBlockN = 64;
+
+// Byte offset of acc in a split-key workspace, and its total size; false if
+// the sizes overflow.
+bool splitkv_layout(int64_t rows, int d, int num_splits, size_t &acc_off, size_t &total)
+{
+    const double bytes = (double)num_splits * rows * (d + 2) * sizeof(float) + 256.0;
+    if (bytes > 9.0e18) return false;
+    const size_t ml = (size_t)num_splits * rows * 2 * sizeof(float);
+    acc_off = (ml + 255) & ~(size_t)255;
+    total = acc_off + (size_t)num_splits * rows * d * sizeof(float);
+    return true;
+}
+
+int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+             int N_q, int N_k, int d, float scale, int causal, const uint8_t *kv_len_mask,
+             int dtype, void *stream, const fa_opts *opts)
+{
+    Sizes sz;
+    int rc = check_fwd_args(q, k, v, o, lse, B, H, N_q, N_k, d, scale, kv_len_mask, dtype, 1, sz);
+    if (rc != FA_OK) return rc;
+
+    int block_n = opts ? opts->block_n : 0;
+    if (block_n != 0 && block_n != 16 && block_n != 32 && block_n != 64 && block_n != 128)
+        return FA_ERR_TILE;
+    if (block_n == 0) block_n = 64;
+
+    float *trace = opts ? opts->trace : nullptr;
+    if (trace) {
+        if (opts->trace_b < 0 || opts->trace_b >= B || opts->trace_h < 0 || opts->trace_h >= H ||
+            opts->trace_row < 0 || opts->trace_row >= N_q)
+            return FA_ERR_ARG;
+        const size_t tb = (size_t)((N_k + block_n - 1) / block_n) * 4 * sizeof(float);
+        if (overlaps_fwd(trace, tb, q, k, v, o, lse, kv_len_mask, sz)) return FA_ERR_ALIAS;
+    }
+
+    rc = check_device();
+    if (rc != FA_OK) return rc;
+
+    fa::Params p = make_params(q, k, v, o, lse, H, N_q, N_k, scale, kv_len_mask);
+    p.reverse = (opts && opts->reverse_kv) ? 1 : 0;
+    if (trace) {
+        p.trace = trace;
+        p.trace_bh = opts->trace_b * H + opts->trace_h;
+        p.trace_row = opts->trace_row;
+    }
+    return launch_status(fa::launch_fwd(p, dtype, d, block_n, causal ? 1 : 0, B, H,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -131,6 +197,98 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, 
                     stream, opts);
 }
 
+size_t fa_splitkv_workspace_bytes(int B, int H, int N_q, int d, int num_splits)
+{
+    if (B <= 0 || H <= 0 || N_q <= 0 || (d != 64 && d != 128) || num_splits < 1 ||
+        num_splits > kMaxSplits)
+        return 0;
+    size_t acc_off = 0, total = 0;
+    if (!splitkv_layout((int64_t)B * H * N_q, d, num_splits, acc_off, total)) return 0;
+    return total;
+}
+
+int fa_splitkv_splits(int B, int H, int N_q, int N_k, int d, int causal)
+{
+    if (B <= 0 || H <= 0 || N_q <= 0 || N_k <= 0) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+    int rc = check_device();
+    if (rc != FA_OK) return rc;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    // Four workgroups per compute unit keep two resident on each with work
+    // queued behind them.
+    const double target = 4.0 * cus;
+    const double wgs = (double)B * H * (((int64_t)N_q + 127) / 128);
+    if (wgs >= target) return 1;
+    const int64_t keys = causal ? (N_q < N_k ? N_q : N_k) : N_k;
+    const int64_t tiles = (keys + kSplitBlockN - 1) / kSplitBlockN;
+    int64_t s = (int64_t)std::ceil(target / wgs);
+    const int64_t by_tiles = tiles / 4 > 1 ? tiles / 4 : 1;   // at least 4 tiles per range
+    if (s > by_tiles) s = by_tiles;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return (int)(s < 1 ? 1 : s);
+}
+
+int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                   int H, int N_q, int N_k, int d, float scale, int causal,
+                   const uint8_t *kv_len_mask, int dtype, int num_splits, void *workspace,
+                   size_t workspace_bytes, void *stream)
+{
+    Sizes sz;
+    const int ns = (num_splits >= 1 && num_splits <= kMaxSplits) ? num_splits : 1;
+    int rc = check_fwd_args(q, k, v, o, lse, B, H, N_q, N_k, d, scale, kv_len_mask, dtype, ns, sz);
+    if (rc != FA_OK) return rc;
+    if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_ARG;
+    size_t acc_off = 0, total = 0;
+    if (!splitkv_layout(sz.rows, d, num_splits, acc_off, total)) return FA_ERR_SHAPE;
+    if (!workspace || workspace_bytes < total || (reinterpret_cast<uintptr_t>(workspace) & 15))
+        return FA_ERR_WORKSPACE;
+    if (overlaps_fwd(workspace, total, q, k, v, o, lse, kv_len_mask, sz)) return FA_ERR_ALIAS;
+
+    rc = check_device();
+    if (rc != FA_OK) return rc;
+
+    fa::Params p = make_params(q, k, v, o, lse, H, N_q, N_k, scale, kv_len_mask);
+    float *ws = static_cast<float *>(workspace);
+    p.n_split = num_splits;
+    p.part_rows = sz.rows;
+    p.part_m = ws;
+    p.part_l = ws + (size_t)num_splits * sz.rows;
+    p.part_o = reinterpret_cast<float *>(static_cast<char *>(workspace) + acc_off);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    rc = launch_status(fa::launch_fwd(p, dtype, d, kSplitBlockN, causal ? 1 : 0, B, H, st));
+    if (rc != FA_OK) return rc;
+    return launch_status(fa::launch_merge(p.part_m, p.part_l, p.part_o, num_splits, sz.rows, d,
+                                          scale, o, lse, dtype, st));
+}
+
+int fa_merge_states(const float *m, const float *l, const float *acc, int n_parts, int64_t rows,
+                    int d, float scale, void *o, float *lse, int dtype, void *stream)
+{
+    if (!m || !l || !acc || !o || !lse) return FA_ERR_NULL;
+    if (rows <= 0) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_SCALE;
+    if (n_parts < 1) return FA_ERR_ARG;
+    if ((double)n_parts * rows * d * sizeof(float) > 9.0e18) return FA_ERR_SHAPE;
+    const size_t mlb = (size_t)n_parts * rows * sizeof(float);
+    const size_t ab = mlb * d;
+    const size_t ob = (size_t)rows * d * (dtype == FA_DTYPE_BF16 ? 2 : 4);
+    const size_t lb = (size_t)rows * sizeof(float);
+    if (overlaps(o, ob, m, mlb) || overlaps(o, ob, l, mlb) || overlaps(o, ob, acc, ab) ||
+        overlaps(lse, lb, m, mlb) || overlaps(lse, lb, l, mlb) || overlaps(lse, lb, acc, ab) ||
+        overlaps(o, ob, lse, lb))
+        return FA_ERR_ALIAS;
+    int rc = check_device();
+    if (rc != FA_OK) return rc;
+    return launch_status(fa::launch_merge(m, l, acc, n_parts, rows, d, scale, o, lse, dtype,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 const char *fa_strerror(int code)
 {
     const char *base;
@@ -144,7 +302,13 @@ const char *fa_strerror(int code)
     case FA_ERR_TILE: base = "block_n must be 0, 16, 32, 64 or 128"; break;
     case FA_ERR_DEVICE: base = "the current HIP device is not a gfx950 GPU"; break;
     case FA_ERR_LAUNCH: base = "HIP rejected the kernel launch"; break;
-    case FA_ERR_ALIAS: base = "o or lse overlaps an input buffer"; break;
+    case FA_ERR_ALIAS: base = "an output overlaps an input or another output"; break;
+    case FA_ERR_ARG:
+        base = "argument out of range (traced row, num_splits or n_parts)";
+        break;
+    case FA_ERR_WORKSPACE:
+        base = "workspace is NULL, not 16-byte aligned, or smaller than required";
+        break;
     default: base = "unknown status code"; break;
     }
     if ((code == FA_ERR_LAUNCH || code == FA_ERR_DEVICE) && g_last_hip != hipSuccess) {

@@ -22,11 +22,31 @@ struct Params {
     float c;              // scale * log2(e): scores to the exp2 domain
     float scale;
     int reverse;          // visit key tiles last to first
+    // Split-key mode: each query tile's key tiles are cut into n_split
+    // consecutive ranges, one workgroup each, and every row's partial state
+    // (m in raw score units, l, o~) goes to part_m / part_l / part_o
+    // ([n_split][part_rows], same, [n_split][part_rows][d]) instead of o and
+    // lse.  n_split = 1 and null pointers: the plain pass.
+    int n_split;
+    int64_t part_rows;    // B * H * N_q
+    float *part_m;
+    float *part_l;
+    float *part_o;
+    // Per-tile state of one row (fa_opts.trace), or nullptr.
+    float *trace;
+    int trace_bh;         // b * H + h of the traced row
+    int trace_row;        // its query index
 };
 
 // Enqueues the forward kernel for validated arguments.  dtype: 0 = fp32,
 // 1 = bf16; d: 64 or 128; block_n: 16, 32, 64 or 128.
 hipError_t launch_fwd(const Params &p, int dtype, int d, int block_n, int causal, int B, int H,
                       hipStream_t stream);
+
+// Enqueues the merge of n_parts partial states per row (part-major layout of
+// fa_merge_states) into o (dtype 0 = fp32, 1 = bf16) and lse.
+hipError_t launch_merge(const float *m, const float *l, const float *acc, int n_parts,
+                        int64_t rows, int d, float scale, void *o, float *lse, int dtype,
+                        hipStream_t stream);
 
 }  // namespace fa

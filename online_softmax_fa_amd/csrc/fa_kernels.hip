@@ -279,16 +279,22 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
 // Per-thread state and steps of the bf16 kernel.  The kernel body is a
-// struct with device member functions (no lambdas), all inlined.
-template <int D, int BN, int NW, bool CAUSAL>
+// struct with device member functions (no lambdas), all inlined.  TRACE
+// builds the variant that records one row's state after every tile
+// (fa_opts.trace); the other variant carries no trace code at all.
+template <int D, int BN, int NW, bool CAUSAL, bool TRACE>
 struct Bf16Fwd {
     using C = Bf16Cfg<D, BN, NW>;
 
     lds_char *lds;
     int lane, w, l31, h;
-    int bh, b, q0, qw0, qrow, Nq, Nk, n_t;
+    int bh, b, q0, qw0, qrow, Nq, Nk;
+    int split, t_lo, n_t;   // key-range split of this workgroup: tiles t_lo .. t_lo + n_t - 1
     bool reverse;
+    bool trace_on;          // this wave holds the traced row
     float c;
+    float *trace;
+    int trace_row;
     const uint16_t *Kg, *Vg;
     const uint8_t *Mg;
 
@@ -314,9 +320,12 @@ struct Bf16Fwd {
         l31 = lane & 31;
         h = lane >> 5;
 
+        // work item L = (head, query tile, key range), key ranges innermost
         const int L = logical_tile(blockIdx.x, gridDim.x);
-        bh = L / p.n_qt;
-        const int qt = CAUSAL ? (p.n_qt - 1 - L % p.n_qt) : (L % p.n_qt);
+        split = L % p.n_split;
+        const int L2 = L / p.n_split;
+        bh = L2 / p.n_qt;
+        const int qt = CAUSAL ? (p.n_qt - 1 - L2 % p.n_qt) : (L2 % p.n_qt);
         b = bh / p.H;
         q0 = qt * C::BM;
         qw0 = q0 + 32 * w;          // first query row of this wave
@@ -325,6 +334,9 @@ struct Bf16Fwd {
         Nk = p.Nk;
         c = p.c;
         reverse = p.reverse != 0;
+        trace = p.trace;
+        trace_row = p.trace_row;
+        trace_on = TRACE && bh == p.trace_bh && p.trace_row >= qw0 && p.trace_row < qw0 + 32;
 
         const uint16_t *Qg = static_cast<const uint16_t *>(p.q) + (size_t)bh * Nq * D;
         Kg = static_cast<const uint16_t *>(p.k) + (size_t)bh * Nk * D;
@@ -340,13 +352,16 @@ struct Bf16Fwd {
         for (int kk = 0; kk < D / 16; ++kk)
             qf[kk] = *reinterpret_cast<const bf16x8 *>(src + 16 * kk);
 
-        // Number of key tiles this workgroup needs.
-        n_t = (Nk + BN - 1) / BN;
+        // Key tiles the query tile needs (under causality, up to the diagonal
+        // of its last row), and this workgroup's range of them.
+        int n_all = (Nk + BN - 1) / BN;
         if (CAUSAL) {
             const int last_q = (q0 + C::BM < Nq ? q0 + C::BM : Nq) - 1;
             const int need = last_q / BN + 1;
-            n_t = need < n_t ? need : n_t;
+            n_all = need < n_all ? need : n_all;
         }
+        t_lo = (int)((int64_t)split * n_all / p.n_split);
+        n_t = (int)((int64_t)(split + 1) * n_all / p.n_split) - t_lo;
 
         // Per-lane LDS byte addresses (stage 0) of the MFMA operands.
         //   K (A operand of S^T = K.Q^T, 16 bytes): key row 32*kb + l31,
@@ -445,22 +460,30 @@ struct Bf16Fwd {
 
     // One iteration: prefetch tile it+1 into the other stage, compute tile it
     // from stage ST, then wait for the prefetch and synchronise.
+    // Key tile visited at step it.
+    __device__ __forceinline__ int tile_at(int it) const
+    {
+        return t_lo + (reverse ? (n_t - 1 - it) : it);
+    }
+
     template <int ST>
     __device__ __forceinline__ void iteration(int it)
     {
-        const int t = reverse ? (n_t - 1 - it) : it;
+        const int t = tile_at(it);
         const bool has_next = it + 1 < n_t;
         if (has_next) {
-            const int tn = reverse ? (n_t - 2 - it) : (it + 1);
+            const int tn = tile_at(it + 1);
             if (Mg) load_mask(tn);
             issue_tile(tn, ST ^ 1);
         }
 
         const int k0 = t * BN;
         const bool tile_empty = Mg && kv_lo == 0 && (BN <= 64 || kv_hi == 0);
-        // Keys beyond this wave's last row are all masked under causality.
-        const bool wave_skip = tile_empty || (CAUSAL && k0 > qw0 + 31);
+        // Keys beyond this wave's last row are all masked under causality;
+        // a wave whose rows all lie past N_q has nothing to compute.
+        const bool wave_skip = tile_empty || (CAUSAL && k0 > qw0 + 31) || qw0 >= Nq;
         if (!wave_skip) compute<ST>(k0);
+        if (TRACE && trace_on) record(it, t);
 
         wait_vmem();
         __syncthreads();
@@ -591,6 +614,37 @@ struct Bf16Fwd {
         }
     }
 
+    // The reference of the row's state in raw score units: mc / c.
+    __device__ __forceinline__ float m_raw() const { return mc == kNegInf ? kNegInf : mc / c; }
+
+    // Trace entry `it`: {tile, m, l, 0} of the traced row after tile t.
+    __device__ __forceinline__ void record(int it, int t)
+    {
+        const float l_row = pair_sum(l_part);
+        if (qrow == trace_row && h == 0) {
+            const f32x4 e = {(float)t, m_raw(), l_row, 0.0f};
+            *reinterpret_cast<f32x4 *>(trace + 4 * (size_t)it) = e;
+        }
+    }
+
+    // Split-key mode: the row's partial state over this key range.
+    __device__ __forceinline__ void write_partial(const Params &p, float l_row)
+    {
+        const size_t row = (size_t)split * p.part_rows + (size_t)bh * Nq + qrow;
+        float *Og = p.part_o + row * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 x = {o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
+                *reinterpret_cast<f32x4 *>(Og + 32 * db + 8 * g + 4 * h) = x;
+            }
+        if (h == 0) {
+            p.part_m[row] = m_raw();
+            p.part_l[row] = l_row;
+        }
+    }
+
     // o = o~ / l, lse = m + ln l; a row with no visible key gets o = 0 and
     // lse = -inf.
     __device__ __forceinline__ void epilogue(const Params &p)
@@ -598,6 +652,10 @@ struct Bf16Fwd {
         const float l_row = pair_sum(l_part);
         const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
         if (qrow >= Nq) return;
+        if (p.part_o) {
+            write_partial(p, l_row);
+            return;
+        }
         uint16_t *Og = static_cast<uint16_t *>(p.o) + ((size_t)bh * Nq + qrow) * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -631,16 +689,16 @@ constexpr int bf16_blocks_per_cu(int d, int bn, int nw)
     return b < 1 ? 1 : b;
 }
 
-template <int D, int BN, int NW, bool CAUSAL>
+template <int D, int BN, int NW, bool CAUSAL, bool TRACE>
 __global__ __launch_bounds__(NW * 64, bf16_blocks_per_cu(D, BN, NW)) void fa_fwd_bf16_kernel(
     const Params p)
 {
     extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
-    Bf16Fwd<D, BN, NW, CAUSAL> k;
+    Bf16Fwd<D, BN, NW, CAUSAL, TRACE> k;
     k.init(p, (lds_char *)lds_raw);
 
     if (k.n_t > 0) {
-        const int t0 = k.reverse ? k.n_t - 1 : 0;
+        const int t0 = k.tile_at(0);
         if (k.Mg) k.load_mask(t0);
         k.issue_tile(t0, 0);
     }
@@ -674,7 +732,80 @@ struct F32Cfg {
     static constexpr size_t LDS_BYTES = 2 * K_ELEMS * sizeof(float);
 };
 
+// One key tile of the fp32 kernel for the 32 query rows of a wave: scores,
+// masks, the recurrence step (online_step) and the P.V products.
 template <int D, int BN, int NW, bool CAUSAL>
+__device__ __forceinline__ void f32_tile(const float *Kl, const float *Vl, const f32x4 (&qf)[D / 8],
+                                         int k0, int Nk, int qw0, int qrow, int l31, int h,
+                                         const uint8_t *Mg, uint64_t kv_lo, uint64_t kv_hi,
+                                         float c, float &m_raw, float &l_part,
+                                         f32x16 (&o)[D / 32])
+{
+    using C = F32Cfg<D, BN, NW>;
+    f32x16 s[C::NKB];
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+#pragma unroll
+    for (int g = 0; g < D / 8; ++g)
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(
+                Kl + (32 * kb + l31) * C::P + 8 * g + 4 * h);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], qf[g][i], s[kb], 0, 0, 0);
+        }
+
+    const bool kv_partial = Mg && !(kv_lo == ~0ull && (BN <= 64 || kv_hi == ~0ull));
+    const bool tail = k0 + C::BNA > Nk || BN < 32;
+    const bool diag = CAUSAL && (k0 + BN - 1 > qw0);
+    if (kv_partial || tail || diag) {
+        uint32_t vis[C::NKB];
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+            const int first = k0 + 32 * kb + 4 * h;
+            int lim = (BN < 32 ? k0 + BN : Nk) - first;
+            if (BN < 32 && Nk - first < lim) lim = Nk - first;
+            if (CAUSAL && qrow - first + 1 < lim) lim = qrow - first + 1;
+            uint32_t bits = prefix_bits(lim);
+            if (Mg) {
+                const uint64_t word = (kb < 2) ? kv_lo : kv_hi;
+                bits &= (uint32_t)(word >> (32 * (kb & 1) + 4 * h));
+            }
+            vis[kb] = bits;
+        }
+        apply_visibility<C::NKB>(s, vis);
+    }
+
+    const float alpha = online_step<C::NKB>(s, m_raw, l_part, c);
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+
+    // O^T += V^T . P^T: the MFMA fed by weight register r contracts over
+    // the two keys 32kb + kpos(r) (lanes 0-31) and 32kb + kpos(r) + 4
+    // (lanes 32-63); the V operand of lane l is V[that key][32db + l%32].
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            // keys 16..31 of a 16-key tile are phantoms (registers 8..15)
+            if (BN < 32 && r >= 8) continue;
+            const int key = 32 * kb + kpos(r) + 4 * h;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const float a = Vl[key * C::P + 32 * db + l31];
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[kb][r], o[db], 0, 0, 0);
+            }
+        }
+}
+
+template <int D, int BN, int NW, bool CAUSAL, bool TRACE>
 __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_f32_kernel(const Params p)
 {
     using C = F32Cfg<D, BN, NW>;
@@ -686,10 +817,12 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_f32_kernel(const Params p)
     const int l31 = lane & 31;
     const int h = lane >> 5;
 
-    const int G = gridDim.x;
-    const int L = logical_tile(blockIdx.x, G);
-    const int bh = L / p.n_qt;
-    const int qt = CAUSAL ? (p.n_qt - 1 - L % p.n_qt) : (L % p.n_qt);
+    // work item L = (head, query tile, key range), key ranges innermost
+    const int L = logical_tile(blockIdx.x, gridDim.x);
+    const int split = L % p.n_split;
+    const int L2 = L / p.n_split;
+    const int bh = L2 / p.n_qt;
+    const int qt = CAUSAL ? (p.n_qt - 1 - L2 % p.n_qt) : (L2 % p.n_qt);
     const int b = bh / p.H;
     const int q0 = qt * C::BM;
     const int qw0 = q0 + 32 * w;
@@ -711,12 +844,16 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_f32_kernel(const Params p)
             qf[g] = *reinterpret_cast<const f32x4 *>(Qg + (size_t)qr * D + 8 * g + 4 * h);
     }
 
-    int n_t = (Nk + BN - 1) / BN;
+    // Key tiles the query tile needs, and this workgroup's range of them.
+    int n_all = (Nk + BN - 1) / BN;
     if (CAUSAL) {
         const int last_q = (q0 + C::BM < Nq ? q0 + C::BM : Nq) - 1;
         const int need = last_q / BN + 1;
-        n_t = need < n_t ? need : n_t;
+        n_all = need < n_all ? need : n_all;
     }
+    const int t_lo = (int)((int64_t)split * n_all / p.n_split);
+    const int n_t = (int)((int64_t)(split + 1) * n_all / p.n_split) - t_lo;
+    const bool trace_on = TRACE && bh == p.trace_bh && p.trace_row >= qw0 && p.trace_row < qw0 + 32;
 
     float *Kl = ldsf;
     float *Vl = ldsf + C::K_ELEMS;
@@ -766,14 +903,14 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_f32_kernel(const Params p)
         }
     }
 
-    if (n_t > 0) load_tile(p.reverse ? n_t - 1 : 0);
+    if (n_t > 0) load_tile(t_lo + (p.reverse ? n_t - 1 : 0));
 
     for (int it = 0; it < n_t; ++it) {
-        const int t = p.reverse ? (n_t - 1 - it) : it;
+        const int t = t_lo + (p.reverse ? (n_t - 1 - it) : it);
         __syncthreads();   // every wave is done with the previous tile
         store_tile();
         __syncthreads();
-        if (it + 1 < n_t) load_tile(p.reverse ? (n_t - 2 - it) : (it + 1));
+        if (it + 1 < n_t) load_tile(t_lo + (p.reverse ? (n_t - 2 - it) : (it + 1)));
 
         const int k0 = t * BN;
         uint64_t kv_lo = ~0ull, kv_hi = ~0ull;
@@ -788,74 +925,40 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_f32_kernel(const Params p)
             }
         }
         const bool tile_empty = Mg && kv_lo == 0 && (BN <= 64 || kv_hi == 0);
-        if (tile_empty || (CAUSAL && k0 > qw0 + 31)) continue;
-
-        f32x16 s[C::NKB];
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-#pragma unroll
-        for (int g = 0; g < D / 8; ++g)
-#pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb) {
-                const f32x4 a = *reinterpret_cast<const f32x4 *>(
-                    Kl + (32 * kb + l31) * C::P + 8 * g + 4 * h);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], qf[g][i], s[kb], 0, 0, 0);
+        if (!(tile_empty || (CAUSAL && k0 > qw0 + 31) || qw0 >= Nq))
+            f32_tile<D, BN, NW, CAUSAL>(Kl, Vl, qf, k0, Nk, qw0, qrow, l31, h, Mg, kv_lo, kv_hi, c,
+                                        m_raw, l_part, o);
+        if (TRACE && trace_on) {
+            // trace entry it: {tile, m, l, 0} of the traced row after tile t
+            const float l_row = pair_sum(l_part);
+            if (qrow == p.trace_row && h == 0) {
+                const f32x4 e = {(float)t, m_raw, l_row, 0.0f};
+                *reinterpret_cast<f32x4 *>(p.trace + 4 * (size_t)it) = e;
             }
-
-        const bool kv_partial = Mg && !(kv_lo == ~0ull && (BN <= 64 || kv_hi == ~0ull));
-        const bool tail = k0 + C::BNA > Nk || BN < 32;
-        const bool diag = CAUSAL && (k0 + BN - 1 > qw0);
-        if (kv_partial || tail || diag) {
-            uint32_t vis[C::NKB];
-#pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb) {
-                const int first = k0 + 32 * kb + 4 * h;
-                int lim = (BN < 32 ? k0 + BN : Nk) - first;
-                if (BN < 32 && Nk - first < lim) lim = Nk - first;
-                if (CAUSAL && qrow - first + 1 < lim) lim = qrow - first + 1;
-                uint32_t bits = prefix_bits(lim);
-                if (Mg) {
-                    const uint64_t word = (kb < 2) ? kv_lo : kv_hi;
-                    bits &= (uint32_t)(word >> (32 * (kb & 1) + 4 * h));
-                }
-                vis[kb] = bits;
-            }
-            apply_visibility<C::NKB>(s, vis);
         }
-
-        const float alpha = online_step<C::NKB>(s, m_raw, l_part, c);
-        if (__any(alpha != 1.0f)) {
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-        }
-
-        // O^T += V^T . P^T: the MFMA fed by weight register r contracts over
-        // the two keys 32kb + kpos(r) (lanes 0-31) and 32kb + kpos(r) + 4
-        // (lanes 32-63); the V operand of lane l is V[that key][32db + l%32].
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                // keys 16..31 of a 16-key tile are phantoms (registers 8..15)
-                if (BN < 32 && r >= 8) continue;
-                const int key = 32 * kb + kpos(r) + 4 * h;
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const float a = Vl[key * C::P + 32 * db + l31];
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[kb][r], o[db], 0, 0, 0);
-                }
-            }
     }
 
     const float l_row = pair_sum(l_part);
+    if (qrow >= Nq) return;
+    if (p.part_o) {
+        // split-key mode: the row's partial state over this key range
+        const size_t row = (size_t)split * p.part_rows + (size_t)bh * Nq + qrow;
+        float *Og = p.part_o + row * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 x = {o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
+                *reinterpret_cast<f32x4 *>(Og + 32 * db + 8 * g + 4 * h) = x;
+            }
+        if (h == 0) {
+            p.part_m[row] = m_raw;
+            p.part_l[row] = l_row;
+        }
+        return;
+    }
     const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
-    if (qrow < Nq) {
+    {
         float *Og = static_cast<float *>(p.o) + ((size_t)bh * Nq + qrow) * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -894,17 +997,30 @@ static hipError_t launch(const void *kernel, void (*fn)(Params), std::atomic<uin
     return hipGetLastError();
 }
 
-template <int D, int BN, int NW, bool CAUSAL, bool BF16>
+template <int D, int BN, int NW, bool CAUSAL, bool TRACE, bool BF16>
 static hipError_t launch_instance(int grid, int threads, size_t lds, hipStream_t stream,
                                   const Params &p)
 {
     static std::atomic<uint64_t> done{0};
     void (*fn)(Params);
     if constexpr (BF16)
-        fn = fa_fwd_bf16_kernel<D, BN, NW, CAUSAL>;
+        fn = fa_fwd_bf16_kernel<D, BN, NW, CAUSAL, TRACE>;
     else
-        fn = fa_fwd_f32_kernel<D, BN, NW, CAUSAL>;
+        fn = fa_fwd_f32_kernel<D, BN, NW, CAUSAL, TRACE>;
     return launch(reinterpret_cast<const void *>(fn), fn, done, grid, threads, lds, stream, p);
+}
+
+// The four (causal, trace) variants of one kernel configuration.
+template <int D, int BN, int NW, bool BF16>
+static hipError_t launch_variant(int causal, int grid, int threads, size_t lds,
+                                 hipStream_t stream, const Params &p)
+{
+    const bool trace = p.trace != nullptr;
+    if (causal)
+        return trace ? launch_instance<D, BN, NW, true, true, BF16>(grid, threads, lds, stream, p)
+                     : launch_instance<D, BN, NW, true, false, BF16>(grid, threads, lds, stream, p);
+    return trace ? launch_instance<D, BN, NW, false, true, BF16>(grid, threads, lds, stream, p)
+                 : launch_instance<D, BN, NW, false, false, BF16>(grid, threads, lds, stream, p);
 }
 
 template <int D, int BN>
@@ -914,10 +1030,8 @@ static hipError_t dispatch_bf16(const Params &p0, int causal, int B, int H, hipS
     using C = Bf16Cfg<D, BN, NW>;
     Params p = p0;
     p.n_qt = (p.Nq + C::BM - 1) / C::BM;
-    const int grid = B * H * p.n_qt;
-    if (causal)
-        return launch_instance<D, BN, NW, true, true>(grid, C::T, C::LDS_BYTES, stream, p);
-    return launch_instance<D, BN, NW, false, true>(grid, C::T, C::LDS_BYTES, stream, p);
+    const int grid = B * H * p.n_qt * p.n_split;
+    return launch_variant<D, BN, NW, true>(causal, grid, C::T, C::LDS_BYTES, stream, p);
 }
 
 template <int D, int BN>
@@ -927,10 +1041,8 @@ static hipError_t dispatch_f32(const Params &p0, int causal, int B, int H, hipSt
     using C = F32Cfg<D, BN, NW>;
     Params p = p0;
     p.n_qt = (p.Nq + C::BM - 1) / C::BM;
-    const int grid = B * H * p.n_qt;
-    if (causal)
-        return launch_instance<D, BN, NW, true, false>(grid, C::T, C::LDS_BYTES, stream, p);
-    return launch_instance<D, BN, NW, false, false>(grid, C::T, C::LDS_BYTES, stream, p);
+    const int grid = B * H * p.n_qt * p.n_split;
+    return launch_variant<D, BN, NW, false>(causal, grid, C::T, C::LDS_BYTES, stream, p);
 }
 
 template <int D>
@@ -958,6 +1070,103 @@ hipError_t launch_fwd(const Params &p, int dtype, int d, int block_n, int causal
 {
     if (d == 64) return dispatch_d<64>(p, dtype, block_n, causal, B, H, stream);
     return dispatch_d<128>(p, dtype, block_n, causal, B, H, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Merge of partial states.  Every state of a row is rewritten to the common
+// reference M = max_i m_i by the rescaling identity -- l_i and acc_i times
+// exp(scale * (m_i - M)) <= 1 -- and the rewritten sums add ("The math of
+// FlashAttention", "The rescaling identity, derived"; "Proof of exactness":
+// the order of the key ranges does not matter).  Then o = acc / l and
+// lse = M * scale + ln l; o = 0 and lse = -inf when no part saw a visible key.
+//
+// D/4 threads per row, each owning 4 consecutive columns: the m and l reads
+// of a row are the same addresses for all of its threads (one cache line),
+// the acc reads and the o writes are 16 bytes per lane and contiguous across
+// the row.  The kernel is bound by reading acc once.
+// ---------------------------------------------------------------------------
+struct MergeParams {
+    const float *m;
+    const float *l;
+    const float *acc;
+    void *o;
+    float *lse;
+    int64_t rows;
+    int n_parts;
+    float c;        // scale * log2(e)
+    float scale;
+};
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void fa_merge_kernel(const MergeParams p)
+{
+    constexpr int TPR = D / 4;          // threads per row
+    constexpr int RPB = 256 / TPR;      // rows per workgroup pass
+    const int j = 4 * (threadIdx.x % TPR);
+    for (int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR; row < p.rows;
+         row += (int64_t)gridDim.x * RPB) {
+        float big_m = kNegInf;
+        for (int i = 0; i < p.n_parts; ++i) big_m = fmaxf(big_m, p.m[(size_t)i * p.rows + row]);
+        float l = 0.0f;
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (big_m != kNegInf) {
+            for (int i = 0; i < p.n_parts; ++i) {
+                const size_t pr = (size_t)i * p.rows + row;
+                const float mi = p.m[pr];
+                if (mi == kNegInf) continue;          // no visible key in this part
+                const float alpha = __builtin_amdgcn_exp2f((mi - big_m) * p.c);
+                l = __builtin_fmaf(alpha, p.l[pr], l);
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(p.acc + pr * D + j);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(alpha, a[e], acc[e]);
+            }
+        }
+        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+        if (BF16) {
+            u32x2 pk;
+            pk[0] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc[0] * inv)) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc[1] * inv)) << 16);
+            pk[1] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc[2] * inv)) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc[3] * inv)) << 16);
+            *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(p.o) + (size_t)row * D + j) = pk;
+        } else {
+            const f32x4 x = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+            *reinterpret_cast<f32x4 *>(static_cast<float *>(p.o) + (size_t)row * D + j) = x;
+        }
+        if (j == 0)
+            p.lse[row] = l > 0.0f ? __builtin_fmaf(big_m, p.scale, __builtin_amdgcn_logf(l) * kLn2)
+                                  : kNegInf;
+    }
+}
+
+template <int D, bool BF16>
+static hipError_t launch_merge_d(const MergeParams &p, hipStream_t stream)
+{
+    constexpr int RPB = 256 / (D / 4);
+    const int64_t want = (p.rows + RPB - 1) / RPB;
+    const int grid = (int)(want < 65536 ? want : 65536);
+    void (*fn)(MergeParams) = fa_merge_kernel<D, BF16>;
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(const float *m, const float *l, const float *acc, int n_parts,
+                        int64_t rows, int d, float scale, void *o, float *lse, int dtype,
+                        hipStream_t stream)
+{
+    MergeParams p;
+    p.m = m;
+    p.l = l;
+    p.acc = acc;
+    p.o = o;
+    p.lse = lse;
+    p.rows = rows;
+    p.n_parts = n_parts;
+    p.c = (float)((double)scale * 1.4426950408889634073599);   // as the forward kernels
+    p.scale = scale;
+    if (d == 64)
+        return dtype == 1 ? launch_merge_d<64, true>(p, stream) : launch_merge_d<64, false>(p, stream);
+    return dtype == 1 ? launch_merge_d<128, true>(p, stream) : launch_merge_d<128, false>(p, stream);
 }
 
 }  // namespace fa

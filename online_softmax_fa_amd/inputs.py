@@ -19,6 +19,8 @@ Workloads (shapes, value distributions and masks):
   headline   B=2 H=32 N=8192 d=128 bf16 causal, Q/K/V ~ N(0,1)
   long       B=1 H=8 N=32768 d=128 bf16 non-causal, Q/K/V ~ N(0, 0.5^2),
              plus per-batch key lengths uniform in [N/2, N] as a prefix mask
+  decode     B=8 H=8 N_q=1 N_k=32768 d=128 bf16 non-causal, N(0, 0.5^2): one
+             new query per sequence over the long-context geometry
 """
 
 import math
@@ -31,6 +33,10 @@ WORKLOADS = {
     "mid": dict(B=4, H=16, N=2048, d=64, dtype="bf16", causal=True, std=1.0, seed=1003),
     "headline": dict(B=2, H=32, N=8192, d=128, dtype="bf16", causal=True, std=1.0, seed=1004),
     "long": dict(B=1, H=8, N=32768, d=128, dtype="bf16", causal=False, std=0.5, seed=1005),
+    # one new query per sequence over the long-context cache geometry (8 heads,
+    # 32768 keys, d = 128, N(0, 0.5^2)), 8 sequences: the split-key path
+    "decode": dict(B=8, H=8, N=32768, Nq=1, d=128, dtype="bf16", causal=False, std=0.5,
+                   seed=1006),
 }
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -88,9 +94,10 @@ def workload(name, dtype=None, seed=None):
         w["dtype"] = dtype
     if seed is not None:
         w["seed"] = seed
-    q, k, v = gaussian_qkv(w["B"], w["H"], w["N"], w["N"], w["d"], w["seed"], w["std"], w["dtype"])
+    nq = w.get("Nq", w["N"])
+    q, k, v = gaussian_qkv(w["B"], w["H"], nq, w["N"], w["d"], w["seed"], w["std"], w["dtype"])
     return dict(q=q, k=k, v=v, scale=default_scale(w["d"]), causal=w["causal"], mask=None,
-                dtype=w["dtype"], std=w["std"], **{k2: w[k2] for k2 in ("B", "H", "N", "d")})
+                dtype=w["dtype"], std=w["std"], Nq=nq, **{k2: w[k2] for k2 in ("B", "H", "N", "d")})
 
 
 # ---------------------------------------------------------------------------

@@ -29,12 +29,15 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["fa_fwd", "fa_fwd_ex", "fa_strerror"]
+    assert _declared_functions() == ["fa_fwd", "fa_fwd_ex", "fa_fwd_splitkv", "fa_merge_states",
+                                     "fa_splitkv_splits", "fa_splitkv_workspace_bytes",
+                                     "fa_strerror"]
 
 
 def test_header_compiles_as_c_and_cxx(tmp_path):
     src = tmp_path / "use.c"
-    src.write_text('#include "fa.h"\nint main(void){fa_opts o={0,0};(void)o;'
+    src.write_text('#include "fa.h"\nint main(void){fa_opts o={0,0,0,0,0,0};(void)o;'
+                   'size_t n=fa_splitkv_workspace_bytes(1,1,1,64,1);(void)n;'
                    'return fa_fwd(0,0,0,0,0,1,1,1,1,64,1.0f,0,0,FA_DTYPE_BF16,0)==FA_ERR_NULL?0:1;}\n')
     for comp, std in (("gcc", "-std=c99"), ("g++", "-std=c++17")):
         subprocess.run([comp, std, "-fsyntax-only", "-Wall", "-Werror", "-I",
@@ -52,7 +55,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_strerror_covers_every_code(lib):
-    for code in range(0, -10, -1):
+    for code in range(0, -12, -1):
         s = fa.fa_strerror(code)
         assert s and s != "unknown status code", code
     assert fa.fa_strerror(-99) == "unknown status code"
@@ -66,9 +69,9 @@ FAKE5 = 0x80000000
 
 
 def _call(q=FAKE, k=FAKE2, v=FAKE3, o=FAKE4, lse=FAKE5, B=1, H=1, Nq=8, Nk=8, d=64, scale=0.125,
-          causal=0, mask=None, dtype=1, block_n=0):
+          causal=0, mask=None, dtype=1, block_n=0, trace=None, tb=0, th=0, trow=0):
     lib = fa.load_library()
-    opts = fa.fa_opts(block_n, 0)
+    opts = fa.fa_opts(block_n, 0, trace, tb, th, trow)
     return lib.fa_fwd_ex(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, mask, dtype, None,
                          ctypes.byref(opts))
 
@@ -85,6 +88,8 @@ def _call(q=FAKE, k=FAKE2, v=FAKE3, o=FAKE4, lse=FAKE5, B=1, H=1, Nq=8, Nk=8, d=
     (dict(block_n=48), fa.FA_ERR_TILE), (dict(block_n=256), fa.FA_ERR_TILE),
     (dict(o=FAKE), fa.FA_ERR_ALIAS), (dict(lse=FAKE3 + 16), fa.FA_ERR_ALIAS),
     (dict(mask=FAKE4 + 1), fa.FA_ERR_ALIAS),
+    (dict(trace=0x90000000, tb=1), fa.FA_ERR_ARG), (dict(trace=0x90000000, th=-1), fa.FA_ERR_ARG),
+    (dict(trace=0x90000000, trow=8), fa.FA_ERR_ARG), (dict(trace=FAKE4 + 8), fa.FA_ERR_ALIAS),
 ])
 def test_argument_errors_before_any_device_work(lib, kw, code):
     assert _call(**kw) == code
@@ -95,6 +100,57 @@ def test_valid_arguments_without_gpu_report_device_error(lib):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert _call() == fa.FA_ERR_DEVICE
+    assert _call(trace=0x90000000, tb=0, th=0, trow=7) == fa.FA_ERR_DEVICE
+    assert _split() == fa.FA_ERR_DEVICE
+    assert _merge() == fa.FA_ERR_DEVICE
+    assert lib.fa_splitkv_splits(1, 8, 1, 32768, 128, 0) == fa.FA_ERR_DEVICE
+
+
+WS = 0xA0000000
+
+
+def _split(B=1, H=2, Nq=8, Nk=8, d=64, ns=3, ws=WS, ws_bytes=None, q=FAKE, o=FAKE4):
+    lib = fa.load_library()
+    if ws_bytes is None:
+        ws_bytes = lib.fa_splitkv_workspace_bytes(B, H, Nq, d, ns if 1 <= ns <= 256 else 1)
+    return lib.fa_fwd_splitkv(q, FAKE2, FAKE3, o, FAKE5, B, H, Nq, Nk, d, 0.125, 0, None, 1, ns,
+                              ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), fa.FA_ERR_NULL), (dict(B=0), fa.FA_ERR_SHAPE), (dict(d=80), fa.FA_ERR_HEAD_DIM),
+    (dict(ns=0), fa.FA_ERR_ARG), (dict(ns=257), fa.FA_ERR_ARG), (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=64), fa.FA_ERR_WORKSPACE), (dict(ws=WS + 4), fa.FA_ERR_WORKSPACE),
+    (dict(ws=FAKE4 - 16), fa.FA_ERR_ALIAS), (dict(ws=FAKE), fa.FA_ERR_ALIAS),
+])
+def test_splitkv_argument_errors(lib, kw, code):
+    assert _split(**kw) == code
+
+
+def test_splitkv_workspace_bytes_follow_the_documented_layout(lib):
+    """m and l: float[S][rows] each; acc: float[S][rows][d] from the next
+    multiple of 256 bytes."""
+    for (B, H, Nq, d, S) in ((1, 8, 1, 128, 128), (2, 3, 5, 64, 7), (1, 1, 1, 64, 1)):
+        rows = B * H * Nq
+        acc_off = (2 * S * rows * 4 + 255) // 256 * 256
+        assert lib.fa_splitkv_workspace_bytes(B, H, Nq, d, S) == acc_off + S * rows * d * 4
+    for bad in ((0, 1, 1, 64, 1), (1, 1, 1, 96, 1), (1, 1, 1, 64, 0), (1, 1, 1, 64, 257)):
+        assert lib.fa_splitkv_workspace_bytes(*bad) == 0
+
+
+def _merge(m=FAKE, l=FAKE2, acc=FAKE3, n=4, rows=10, d=64, scale=0.5, o=FAKE4, lse=FAKE5, dt=1):
+    return fa.load_library().fa_merge_states(m, l, acc, n, rows, d, scale, o, lse, dt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(m=None), fa.FA_ERR_NULL), (dict(lse=None), fa.FA_ERR_NULL), (dict(rows=0), fa.FA_ERR_SHAPE),
+    (dict(d=32), fa.FA_ERR_HEAD_DIM), (dict(dt=3), fa.FA_ERR_DTYPE),
+    (dict(scale=float("nan")), fa.FA_ERR_SCALE), (dict(n=0), fa.FA_ERR_ARG),
+    (dict(o=FAKE2 + 64), fa.FA_ERR_ALIAS), (dict(lse=FAKE3 + 4), fa.FA_ERR_ALIAS),
+    (dict(lse=FAKE4 + 64), fa.FA_ERR_ALIAS),
+])
+def test_merge_argument_errors(lib, kw, code):
+    assert _merge(**kw) == code
 
 
 def test_binding_raises_with_the_message(lib):
@@ -126,4 +182,6 @@ def test_every_kernel_has_its_host_stub():
     undefined = [l for l in out.splitlines() if " U " in l and "fa::" in l]
     assert not undefined, undefined
     defined = [l for l in out.splitlines() if "fa::fa_fwd_" in l and "_kernel<" in l]
-    assert len(defined) >= 32, len(defined)
+    assert len(defined) >= 64, len(defined)
+    merge = [l for l in out.splitlines() if "__device_stub__fa_merge_kernel<" in l]
+    assert len(merge) == 4, merge

@@ -1,0 +1,136 @@
+"""GPU per-tile trace of one row (fa_opts.trace) against the oracle's
+block-by-block recurrence.
+
+The tiled-attention interview answer recommends printing (m, l) after every
+block when debugging; the kernel writes {tile, m, l, 0} for one chosen row
+after each key tile it visits.  With exact scores (the adversarial heads) the
+fp32 kernel's m must equal the oracle's running maximum and its l the oracle's
+l ("2.2b", "The Complete Online Softmax Algorithm"), for every tile size, both
+traversal orders and the causal diagonal.  The bf16 kernel states l against a
+reference that may lag the maximum, so it is compared through the running log
+of the sum of exponentials, m*scale + ln l, which any reference gives alike,
+and its reference is checked against the documented lag bound.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.online import online_attention_row
+from online_softmax_fa_amd import inputs
+import online_softmax_fa_amd as fa
+from _parity import say, to_np32
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+LOG2E = 1.4426950408889634
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    fa.load_library()
+
+
+def _tiles_visited(row, N, bn, causal, bm=128):
+    """Key tiles the row's workgroup visits: all of them, or under causality
+    those up to the diagonal of the last row of its 128-row query tile."""
+    n = (N + bn - 1) // bn
+    if causal:
+        q0 = row // bm * bm
+        n = min(n, (min(q0 + bm, N) - 1) // bn + 1)
+    return n
+
+
+def _trace(qd, kd, vd, scale, causal, mask, bn, rev, b, h, row):
+    N = kd.shape[2]
+    buf = torch.full(((N + bn - 1) // bn * 4,), float("nan"), device=DEV)
+    o, lse = fa.attention(qd, kd, vd, scale=scale, causal=causal, kv_len_mask=mask, block_n=bn,
+                          reverse_kv=rev, trace=(buf, b, h, row))
+    torch.cuda.synchronize()
+    return buf.cpu().numpy().reshape(-1, 4), o, lse
+
+
+def _oracle_trace(s_row, vis, bn, n_vis_tiles, rev):
+    keys = min(len(s_row), n_vis_tiles * bn)
+    order = list(range(n_vis_tiles))
+    if rev:
+        order = order[::-1]
+    return online_attention_row(s_row[:keys], None, block=bn, order=order, visible=vis[:keys])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("bn", [16, 32, 64, 128])
+@pytest.mark.parametrize("rev", [False, True])
+def test_trace_of_adversarial_rows(dtype, bn, rev):
+    q, k, v = inputs.adversarial(dtype=dtype)
+    scale = inputs.ADV_SCALE
+    c = scale * LOG2E
+    qn, kn = to_np32(q).astype(np.float64)[0], to_np32(k).astype(np.float64)[0]
+    qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+    N = k.shape[2]
+    cases = inputs.adversarial_cases()
+    for name in ("nomask", "causal", "bern30"):
+        mask, causal = cases[name]
+        md = None if mask is None else mask.to(DEV)
+        for h in (0, 2, 3):
+            for row in (0, 37, 500, N - 1):
+                say("trace %s bn=%d rev=%d %s head %d row %d" % (dtype, bn, rev, name, h, row))
+                tr, _, _ = _trace(qd, kd, vd, scale, causal, md, bn, rev, 0, h, row)
+                n_t = _tiles_visited(row, N, bn, causal)
+                assert np.all(np.isfinite(tr[:n_t, 0])) and np.all(np.isnan(tr[n_t:]))
+                s_row = scale * (kn[h] @ qn[h, row])
+                vis = np.ones(N, bool) if mask is None else mask[0].numpy().astype(bool)
+                if causal:
+                    vis &= np.arange(N) <= row
+                ref = _oracle_trace(s_row, vis, bn, n_t, rev)["trace"]
+                assert [int(t) for t in tr[:n_t, 0]] == [e["block"] for e in ref]
+                for e, (t, m, l, _) in zip(ref, tr[:n_t]):
+                    if e["m_new"] == -math.inf:
+                        assert m == -math.inf and l == 0.0
+                        continue
+                    lse_k = m * scale + math.log(l)
+                    lse_o = e["m_new"] + math.log(e["l"])
+                    if dtype == "f32":
+                        assert m * scale == e["m_new"]            # exact scores, exact max
+                        assert abs(l - e["l"]) <= 1e-5 * e["l"]
+                    else:
+                        m_true = e["m_new"] / scale
+                        slack = 1e-6 * abs(m_true) + 1e-6         # rounding of mc / c
+                        assert m <= m_true + slack
+                        assert m >= m_true - 16.0 / c - slack
+                    assert abs(lse_k - lse_o) <= 1e-5 * max(1.0, abs(lse_o))
+
+
+def test_trace_of_gaussian_causal_rows():
+    """bf16 random inputs at the production tile size: the running log-sum
+    of every visited tile within the lse bar."""
+    B, H, N, d = 1, 2, 2048, 64
+    q, k, v = inputs.gaussian_qkv(B, H, N, N, d, seed=2900, dtype="bf16")
+    scale = inputs.default_scale(d)
+    qn, kn = to_np32(q).astype(np.float64)[0], to_np32(k).astype(np.float64)[0]
+    qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+    for h, row in ((0, 0), (0, 129), (1, 1000), (1, 2047)):
+        tr, _, _ = _trace(qd, kd, vd, scale, True, None, 64, False, 0, h, row)
+        n_t = _tiles_visited(row, N, 64, True)
+        s_row = scale * (kn[h] @ qn[h, row])
+        vis = np.arange(N) <= row
+        ref = _oracle_trace(s_row, vis, 64, n_t, False)["trace"]
+        for e, (t, m, l, _) in zip(ref, tr[:n_t]):
+            if e["m_new"] == -math.inf:
+                assert m == -math.inf and l == 0.0
+            else:
+                assert abs(m * scale + math.log(l) - (e["m_new"] + math.log(e["l"]))) <= 1e-3
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_trace_leaves_the_result_unchanged(dtype):
+    q, k, v = inputs.gaussian_qkv(2, 3, 300, 300, 128, seed=2950, dtype=dtype)
+    qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+    scale = inputs.default_scale(128)
+    o0, lse0 = fa.attention(qd, kd, vd, scale=scale, causal=True)
+    _, o1, lse1 = _trace(qd, kd, vd, scale, True, None, 64, False, 1, 2, 150)
+    assert torch.equal(o0, o1) and torch.equal(lse0, lse1)
