@@ -14,8 +14,17 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
              workload's rows, on this host's cores, in the same unit
 
+With --workload softmax (8192 rows of 8192 fp32 scores) a step is one
+fa_softmax_rows call, reported as HBM GB/s of its compulsory bytes (the rows
+read once and written once).
+
+With --workload decode (8 sequences x 8 heads, one query each over 32768
+keys) a step is one fa_fwd_splitkv call (split-key pass + merge, the
+library's split count), and the line reports HBM GB/s: that workload is
+bound by reading K and V once, so its roofline is the 8 TB/s HBM peak.
+
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--block-n BN] [--no-cpu-baseline] [--cpu-seconds S]
+                       [--block-n BN] [--splits S] [--no-cpu-baseline] [--cpu-seconds S]
        python bench.py --copy-calibration MIB
            runs only a plain device-to-device copy of MIB MiB (3 launches), the
            reference against which hardware byte counters are scaled
@@ -33,6 +42,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X published dense bf16 MFMA peak
 PEAK_F32_TFLOPS = 157.3       # MI355X published fp32 matrix peak
+PEAK_HBM_GBS = 8000.0         # MI355X published HBM3E bandwidth
 
 
 def log(*a):
@@ -41,7 +51,7 @@ def log(*a):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("fa_kernels.hip", "fa_api.cpp", "fa_internal.h"):
+    for f in ("fa_kernels.hip", "fa_softmax.hip", "fa_api.cpp", "fa_internal.h"):
         with open(os.path.join(ROOT, "online_softmax_fa_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -50,6 +60,11 @@ def kernel_source_hash():
 def attention_flops(B, H, Nq, Nk, d, causal):
     f = 4.0 * B * H * Nq * Nk * d
     return f / 2 if causal else f
+
+
+def algorithmic_bytes(B, H, Nq, Nk, d, esz):
+    """Q, K, V read once; O and lse written once."""
+    return B * H * (2 * Nq * d * esz + 2 * Nk * d * esz + Nq * 4)
 
 
 def traffic_from_profile(workload):
@@ -74,11 +89,16 @@ def cpu_baseline(w, seconds):
     oracle.build(force=False)
     q, k, v = (x.float().numpy() for x in (w["q"], w["k"], w["v"]))
     B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    Nq = w["Nq"]
     threads = len(os.sched_getaffinity(0))
-    total_rows = B * H * N
+    total_rows = B * H * Nq
+    hbm = w.get("bound") == "hbm"
+    esz = 2 if w["dtype"] == "bf16" else 4
 
     def row_flops(rows):
-        i = rows % N
+        if hbm:   # the metric's unit: algorithmic bytes of the rows' heads, per row
+            return float(len(rows)) * algorithmic_bytes(B, H, Nq, N, d, esz) / total_rows
+        i = rows % Nq
         keys = (i + 1) if w["causal"] else np.full_like(i, N)
         return float(np.sum(4.0 * d * keys))
 
@@ -99,13 +119,83 @@ def cpu_baseline(w, seconds):
         dt, fl, used = timed(n)
     # the metric's flop count counts a causal run as half of the full square
     return {
-        "value": fl / dt / 1e12,
-        "unit": "TFLOP/s",
+        "value": fl / dt / (1e9 if hbm else 1e12),
+        "unit": "GB/s" if hbm else "TFLOP/s",
         "cores": int(used),
         "kind": "oracle",
         "sample": "%d of %d query rows (evenly spaced over all heads), fp64 three-pass "
                   "oracle, %.1f s wall" % (n, total_rows, dt),
     }
+
+
+def softmax_cpu_baseline(s, seconds):
+    """The fp64 oracle's three-pass softmax on evenly spaced rows, one core
+    (the oracle's row entry point is single-threaded), in GB/s of the rows'
+    compulsory bytes."""
+    import numpy as np
+    import oracle
+
+    oracle.build(force=False)
+    a = s.float().numpy()
+    rows, n = a.shape
+    nb = 2 * n * s.element_size()
+    t0 = time.perf_counter()
+    done = 0
+    for r in np.linspace(0, rows - 1, rows).astype(np.int64):
+        oracle.softmax_row(a[r].astype(np.float64))
+        done += 1
+        if time.perf_counter() - t0 > seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done * nb / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d of %d rows (evenly spaced), fp64 three-pass oracle, %.1f s wall" % (
+                done, rows, dt)}
+
+
+def bench_softmax(args, torch, fa, inputs):
+    dev = torch.device("cuda:0")
+    w = inputs.row_workload(args.workload)
+    rows, n = w["rows"], w["n"]
+    log("workload %s: %d rows x %d %s" % (args.workload, rows, n, w["dtype"]))
+    s = w["s"].to(dev)
+    p = torch.empty_like(s)
+
+    def step():
+        fa.softmax_rows(s, out=p)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    nbytes = 2 * rows * n * s.element_size() + 2 * rows * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log("%.3f ms/step, %.1f GB/s = %.1f%% of %.0f GB/s" % (ms, gbs, 100 * gbs / PEAK_HBM_GBS,
+                                                          PEAK_HBM_GBS))
+    result = {
+        "metric": "online-softmax over score rows, HBM GB/s of the compulsory bytes, 1 MI355X",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w["dtype"], "data": "synthetic",
+        "config": {"workload": "%s: %d rows x %d %s scores ~ N(0,%g^2)" % (
+            args.workload, rows, n, w["dtype"], w["std"]), "rows": rows, "n": n},
+        "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "algorithmic_bytes_per_step": nbytes,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_from_profile(args.workload)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = softmax_cpu_baseline(w["s"], args.cpu_seconds)
+        log("cpu baseline: %s" % result["cpu_baseline"])
+    print(json.dumps(result), flush=True)
 
 
 def main():
@@ -115,6 +205,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--block-n", type=int, default=0)
+    ap.add_argument("--splits", type=int, default=0,
+                    help="decode: split count (0: the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
@@ -140,18 +232,32 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
         return
     fa.load_library()
+    if args.workload in inputs.ROW_WORKLOADS:
+        return bench_softmax(args, torch, fa, inputs)
     dev = torch.device("cuda:0")
     w = inputs.workload(args.workload)
-    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
-    log("workload %s: B=%d H=%d N=%d d=%d %s causal=%d" % (args.workload, B, H, N, d, w["dtype"],
-                                                         w["causal"]))
+    B, H, N, d, Nq = w["B"], w["H"], w["N"], w["d"], w["Nq"]
+    split = args.workload == "decode"
+    w["bound"] = "hbm" if split else "mfma"
+    log("workload %s: B=%d H=%d N_q=%d N_k=%d d=%d %s causal=%d" % (
+        args.workload, B, H, Nq, N, d, w["dtype"], w["causal"]))
     q, k, v = (x.to(dev) for x in (w["q"], w["k"], w["v"]))
     o = torch.empty_like(q)
-    lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    lse = torch.empty(B, H, Nq, dtype=torch.float32, device=dev)
 
-    def step():
-        fa.attention(q, k, v, scale=w["scale"], causal=w["causal"], block_n=args.block_n,
-                     out=(o, lse))
+    if split:
+        ns = args.splits or fa.fa_splitkv_splits(B, H, Nq, N, d, w["causal"])
+        ws = torch.empty(fa.fa_splitkv_workspace_bytes(B, H, Nq, d, ns), dtype=torch.uint8,
+                         device=dev)
+        log("split-key path: %d splits, workspace %d bytes" % (ns, ws.numel()))
+
+        def step():
+            fa.attention_splitkv(q, k, v, scale=w["scale"], causal=w["causal"], num_splits=ns,
+                                 out=(o, lse), workspace=ws)
+    else:
+        def step():
+            fa.attention(q, k, v, scale=w["scale"], causal=w["causal"], block_n=args.block_n,
+                         out=(o, lse))
 
     for _ in range(args.warmup):
         step()
@@ -172,18 +278,34 @@ def main():
     log("timed %d steps: %.3f ms/step (events), %.3f ms/step (wall)" % (
         args.steps, ms, 1e3 * t_wall / args.steps))
 
-    flops = attention_flops(B, H, N, N, d, w["causal"])
+    flops = attention_flops(B, H, Nq, N, d, w["causal"])
     tflops = flops / (ms * 1e-3) / 1e12
-    peak = PEAK_BF16_TFLOPS if w["dtype"] == "bf16" else PEAK_F32_TFLOPS
+    esz = 2 if w["dtype"] == "bf16" else 4
+    nbytes = algorithmic_bytes(B, H, Nq, N, d, esz)
+    gbs = nbytes / (ms * 1e-3) / 1e9
     props = torch.cuda.get_device_properties(dev)
-    log("%.1f TFLOP/s = %.1f%% of %.0f TFLOP/s (%s, %d CUs)" % (
-        tflops, 100 * tflops / peak, peak, props.name, props.multi_processor_count))
+    if split:
+        value, unit, peak, achieved = gbs, "GB/s", PEAK_HBM_GBS, gbs
+        metric = "split-key attention fwd (decode), HBM GB/s of the algorithmic bytes, 1 MI355X"
+        log("%.1f GB/s = %.1f%% of %.0f GB/s; %.2f TFLOP/s (%s, %d CUs)" % (
+            gbs, 100 * gbs / peak, peak, tflops, props.name, props.multi_processor_count))
+    else:
+        peak = PEAK_BF16_TFLOPS if w["dtype"] == "bf16" else PEAK_F32_TFLOPS
+        value, unit, achieved = tflops, "TFLOP/s", tflops
+        metric = "attention fwd TFLOP/s and % of bf16 MFMA peak, 1 MI355X, N=8192 d=128 causal"
+        clk = getattr(props, "clock_rate", 0) or 0     # kHz, as the runtime reports it
+        if clk:
+            log("bf16 dense peak from the device: %d CUs x %.0f MHz x 4096 FLOP/clk = %.1f "
+                "TFLOP/s (published: 2500)" % (props.multi_processor_count, clk / 1e3,
+                                               props.multi_processor_count * clk * 1e3 * 4096 / 1e12))
+        log("%.1f TFLOP/s = %.1f%% of %.0f TFLOP/s (%s, %d CUs)" % (
+            tflops, 100 * tflops / peak, peak, props.name, props.multi_processor_count))
 
     traffic = traffic_from_profile(args.workload)
     result = {
-        "metric": "attention fwd TFLOP/s and % of bf16 MFMA peak, 1 MI355X, N=8192 d=128 causal",
-        "value": round(tflops, 2),
-        "unit": "TFLOP/s",
+        "metric": metric,
+        "value": round(value, 2),
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -194,23 +316,27 @@ def main():
         "dtype": w["dtype"],
         "data": "synthetic",
         "config": {
-            "workload": "%s: B=%d H=%d N_q=N_k=%d d=%d %s %s, Q/K/V ~ N(0,%g^2)" % (
-                args.workload, B, H, N, d, w["dtype"], "causal" if w["causal"] else "non-causal",
-                w["std"]),
-            "B": B, "H": H, "N_q": N, "N_k": N, "d": d, "causal": bool(w["causal"]),
+            "workload": "%s: B=%d H=%d N_q=%d N_k=%d d=%d %s %s, Q/K/V ~ N(0,%g^2)" % (
+                args.workload, B, H, Nq, N, d, w["dtype"],
+                "causal" if w["causal"] else "non-causal", w["std"]),
+            "B": B, "H": H, "N_q": Nq, "N_k": N, "d": d, "causal": bool(w["causal"]),
             "block_n": args.block_n or 64,
         },
-        "pct_of_peak": round(100 * tflops / peak, 2),
+        "pct_of_peak": round(100 * value / peak, 2),
+        "tflops": round(tflops, 3),
+        "algorithmic_bytes_per_step": nbytes,
         "roofline": {
-            "bound": "mfma",
-            "achieved": round(tflops, 2),
+            "bound": "hbm" if split else "mfma",
+            "achieved": round(achieved, 2),
             "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(tflops / peak, 4),
+            "unit": unit,
+            "frac": round(achieved / peak, 4),
             "traffic": traffic,
         },
         "cpu_baseline": None,
     }
+    if split:
+        result["config"]["splits"] = ns
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of rows ...")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

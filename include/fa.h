@@ -243,6 +243,33 @@ int fa_merge_states(const float *m, const float *l, const float *acc, int n_part
                     void *stream);
 
 /*
+ * fa_softmax_rows -- softmax along every row of a score matrix, by the online
+ * recurrence with the values removed ("2.2b: FlashAttention -- Online
+ * Softmax", sections "The Challenge: Computing m and l in Blocks" through
+ * "When Rescaling Actually Happens"): one pass over the row carries the
+ * running maximum m and the running denominator l, rescaling l by
+ * exp(m_old - m_new) whenever m grows; a second pass writes
+ * p_j = exp(s_j - m) / l.  That reads the row twice where the safe softmax
+ * ("The math of FlashAttention", "Safe softmax: the max-subtraction we cannot
+ * give up") reads it three times.
+ *
+ *   s        device [rows, n] scores, `dtype`; -inf marks a masked entry
+ *            (weight exactly 0).  NaN and +inf inputs are out of scope.
+ *   p        device [rows, n] output, `dtype` (bf16 rounded to nearest-even).
+ *            p == s (in place) is allowed; any other overlap is FA_ERR_ALIAS.
+ *   m, l     NULL, or device float[rows]: the row maximum and
+ *            l = sum_j exp(s_j - m)
+ *   rows, n  >= 1 (else FA_ERR_SHAPE)
+ *   dtype    FA_DTYPE_F32 or FA_DTYPE_BF16; arithmetic is float32
+ *
+ * A row whose entries are all -inf gets p = 0, m = -inf and l = 0.  One
+ * workgroup handles one row; rows that are not 16-byte aligned take a slower
+ * element-wise path.
+ */
+int fa_softmax_rows(const void *s, void *p, float *m, float *l, int64_t rows, int64_t n,
+                    int dtype, void *stream);
+
+/*
  * fa_strerror -- a NUL-terminated description of a status code, never NULL.
  * For FA_ERR_LAUNCH and FA_ERR_DEVICE it appends the last HIP error seen by
  * the calling thread; that text lives in a thread-local buffer that stays

@@ -13,6 +13,7 @@ Entry points (same names and meaning as include/fa.h):
   fa_splitkv_splits(B, H, N_q, N_k, d, causal)
   fa_fwd_splitkv(..., dtype, num_splits, workspace, workspace_bytes, stream)
   fa_merge_states(m, l, acc, n_parts, rows, d, scale, o, lse, dtype, stream)
+  fa_softmax_rows(s, p, m, l, rows, n, dtype, stream)
   fa_strerror(code)
 and convenience wrappers that allocate outputs (and workspace) with torch:
   attention(q, k, v, scale=None, causal=False, kv_len_mask=None, block_n=0, reverse_kv=False,
@@ -20,6 +21,7 @@ and convenience wrappers that allocate outputs (and workspace) with torch:
   attention_splitkv(q, k, v, scale=None, causal=False, kv_len_mask=None, num_splits=None,
                     out=None, workspace=None)                       -> (o, lse)
   merge_states(m, l, acc, scale, out_dtype=None, out=None)          -> (o, lse)
+  softmax_rows(s, out=None)                                         -> (p, m, l)
 """
 
 import ctypes
@@ -88,6 +90,8 @@ def load_library(path=LIB_PATH):
                                    sz, vp]
     lib.fa_merge_states.restype = ci
     lib.fa_merge_states.argtypes = [vp, vp, vp, ci, i64, ci, cf, vp, vp, ci, vp]
+    lib.fa_softmax_rows.restype = ci
+    lib.fa_softmax_rows.argtypes = [vp, vp, vp, vp, i64, i64, ci, vp]
     _lib = lib
     return lib
 
@@ -155,6 +159,32 @@ def fa_merge_states(m, l, acc, n_parts, rows, d, scale, o, lse, dtype, stream):
                                         int(d), float(scale), _ptr(o), _ptr(lse), int(dtype),
                                         stream)
     _check(rc)
+
+
+def fa_softmax_rows(s, p, m, l, rows, n, dtype, stream):
+    """C fa_softmax_rows."""
+    rc = load_library().fa_softmax_rows(_ptr(s), _ptr(p), _ptr(m), _ptr(l), int(rows), int(n),
+                                        int(dtype), stream)
+    _check(rc)
+
+
+def softmax_rows(s, out=None):
+    """p, m, l for a float32 or bfloat16 CUDA tensor s whose last dimension is
+    the row: p = softmax(s) along it (same shape and dtype), m the row maxima
+    and l = sum exp(s - m) (float32, shape s.shape[:-1]).  out=s computes p
+    in place."""
+    import torch
+    dt = _dtype_code(s)
+    if not s.is_cuda or not s.is_contiguous() or s.dim() < 1:
+        raise FaError(FA_ERR_SHAPE, "s must be a contiguous GPU tensor")
+    n = s.shape[-1]
+    rows = s.numel() // n if n else 0
+    p = torch.empty_like(s) if out is None else out
+    m = torch.empty(s.shape[:-1], dtype=torch.float32, device=s.device)
+    l = torch.empty(s.shape[:-1], dtype=torch.float32, device=s.device)
+    stream = torch.cuda.current_stream(s.device).cuda_stream
+    fa_softmax_rows(s, p, m, l, rows, n, dt, stream)
+    return p, m, l
 
 
 def _dtype_code(t):

@@ -9,7 +9,7 @@ import sys
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
-SOURCES = [os.path.join(_HERE, "csrc", "fa_kernels.hip"), os.path.join(_HERE, "csrc", "fa_api.cpp")]
+SOURCES = [os.path.join(_HERE, "csrc", f) for f in ("fa_kernels.hip", "fa_softmax.hip", "fa_api.cpp")]
 OUT = os.path.join(_HERE, "libfa.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -26,20 +26,45 @@ FLAGS = [
 ]
 
 
-def build(verbose=False):
-    tmp = OUT + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(_ROOT, "include"), "-I", os.path.join(_HERE, "csrc")]
-    cmd += SOURCES + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
+def _filter(stderr):
     # the host pass does not know the packed-fp32 feature and says so; that is harmless
     noise = "is not a recognized feature for this target"
-    err = "\n".join(x for x in r.stderr.splitlines() if noise not in x)
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed (%d):\n%s" % (r.returncode, err))
-    if err.strip() and verbose:
-        print(err, file=sys.stderr)
+    return "\n".join(x for x in stderr.splitlines() if noise not in x)
+
+
+def build(verbose=False):
+    """Compile every source to an object in parallel, then link libfa.so."""
+    tmp = OUT + ".tmp%d" % os.getpid()
+    inc = ["-I", os.path.join(_ROOT, "include"), "-I", os.path.join(_HERE, "csrc")]
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = "%s.%s.o" % (tmp, os.path.basename(src))
+        cmd = [HIPCC] + compile_flags + inc + ["-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                            text=True)))
+        objs.append(obj)
+    failed = []
+    for src, pr in procs:
+        _, err = pr.communicate()
+        err = _filter(err)
+        if pr.returncode != 0:
+            failed.append("%s (%d):\n%s" % (src, pr.returncode, err))
+        elif err.strip() and verbose:
+            print(err, file=sys.stderr)
+    try:
+        if failed:
+            raise RuntimeError("hipcc failed: " + "\n".join(failed))
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("link failed (%d):\n%s" % (r.returncode, _filter(r.stderr)))
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     os.replace(tmp, OUT)
     return OUT
 

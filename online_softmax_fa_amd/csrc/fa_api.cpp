@@ -289,12 +289,32 @@ int fa_merge_states(const float *m, const float *l, const float *acc, int n_part
                                           static_cast<hipStream_t>(stream)));
 }
 
+int fa_softmax_rows(const void *s, void *p, float *m, float *l, int64_t rows, int64_t n,
+                    int dtype, void *stream)
+{
+    if (!s || !p) return FA_ERR_NULL;
+    if (rows <= 0 || n <= 0) return FA_ERR_SHAPE;
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+    const size_t esz = dtype == FA_DTYPE_BF16 ? 2 : 4;
+    if ((double)rows * n * esz > 9.0e18) return FA_ERR_SHAPE;
+    const size_t sb = (size_t)rows * n * esz, vb = (size_t)rows * sizeof(float);
+    if (p != s && overlaps(p, sb, s, sb)) return FA_ERR_ALIAS;
+    const void *bufs[2] = {s, p};
+    for (int i = 0; i < 2; ++i)
+        if (overlaps(m, vb, bufs[i], sb) || overlaps(l, vb, bufs[i], sb)) return FA_ERR_ALIAS;
+    if (overlaps(m, vb, l, vb)) return FA_ERR_ALIAS;
+    int rc = check_device();
+    if (rc != FA_OK) return rc;
+    return launch_status(fa::launch_softmax_rows(s, p, m, l, rows, n, dtype,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 const char *fa_strerror(int code)
 {
     const char *base;
     switch (code) {
     case FA_OK: base = "success"; break;
-    case FA_ERR_NULL: base = "q, k, v, o or lse is NULL"; break;
+    case FA_ERR_NULL: base = "a required pointer is NULL"; break;
     case FA_ERR_SHAPE: base = "B, H, N_q or N_k is not positive, or the sizes overflow"; break;
     case FA_ERR_HEAD_DIM: base = "head width d must be 64 or 128"; break;
     case FA_ERR_DTYPE: base = "dtype must be FA_DTYPE_F32 or FA_DTYPE_BF16"; break;

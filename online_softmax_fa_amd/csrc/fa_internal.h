@@ -49,4 +49,8 @@ hipError_t launch_merge(const float *m, const float *l, const float *acc, int n_
                         int64_t rows, int d, float scale, void *o, float *lse, int dtype,
                         hipStream_t stream);
 
+// Enqueues the row softmax (fa_softmax_rows) for validated arguments.
+hipError_t launch_softmax_rows(const void *s, void *p, float *m, float *l, int64_t rows,
+                               int64_t n, int dtype, hipStream_t stream);
+
 }  // namespace fa

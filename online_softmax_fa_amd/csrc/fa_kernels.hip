@@ -1083,7 +1083,9 @@ hipError_t launch_fwd(const Params &p, int dtype, int d, int block_n, int causal
 // D/4 threads per row, each owning 4 consecutive columns: the m and l reads
 // of a row are the same addresses for all of its threads (one cache line),
 // the acc reads and the o writes are 16 bytes per lane and contiguous across
-// the row.  The kernel is bound by reading acc once.
+// the row.  Parts are loaded 8 at a time so that few memory round trips
+// remain when there are few rows (decoding); with many rows the kernel is
+// bound by reading acc once.
 // ---------------------------------------------------------------------------
 struct MergeParams {
     const float *m;
@@ -1102,23 +1104,47 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const MergeParams p)
 {
     constexpr int TPR = D / 4;          // threads per row
     constexpr int RPB = 256 / TPR;      // rows per workgroup pass
+    constexpr int CHUNK = 8;            // parts loaded together (one memory round trip)
     const int j = 4 * (threadIdx.x % TPR);
     for (int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR; row < p.rows;
          row += (int64_t)gridDim.x * RPB) {
-        float big_m = kNegInf;
-        for (int i = 0; i < p.n_parts; ++i) big_m = fmaxf(big_m, p.m[(size_t)i * p.rows + row]);
-        float l = 0.0f;
+        // The states are folded in CHUNK at a time with the recurrence itself:
+        // the running reference M moves to the chunk's maximum when that is
+        // larger, and what was accumulated is rescaled by exp(M_old - M_new).
+        float big_m = kNegInf, l = 0.0f;
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (big_m != kNegInf) {
-            for (int i = 0; i < p.n_parts; ++i) {
-                const size_t pr = (size_t)i * p.rows + row;
-                const float mi = p.m[pr];
-                if (mi == kNegInf) continue;          // no visible key in this part
-                const float alpha = __builtin_amdgcn_exp2f((mi - big_m) * p.c);
-                l = __builtin_fmaf(alpha, p.l[pr], l);
-                const f32x4 a = *reinterpret_cast<const f32x4 *>(p.acc + pr * D + j);
+        for (int i0 = 0; i0 < p.n_parts; i0 += CHUNK) {
+            float mi[CHUNK], li[CHUNK];
+            f32x4 ai[CHUNK];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(alpha, a[e], acc[e]);
+            for (int u = 0; u < CHUNK; ++u) {
+                mi[u] = kNegInf;
+                if (i0 + u < p.n_parts) {
+                    const size_t pr = (size_t)(i0 + u) * p.rows + row;
+                    mi[u] = p.m[pr];
+                    li[u] = p.l[pr];
+                    ai[u] = *reinterpret_cast<const f32x4 *>(p.acc + pr * D + j);
+                }
+            }
+            float cm = kNegInf;
+#pragma unroll
+            for (int u = 0; u < CHUNK; ++u) cm = fmaxf(cm, mi[u]);
+            if (cm == kNegInf) continue;              // no visible key in this chunk
+            if (cm > big_m) {
+                const float alpha = big_m == kNegInf ? 0.0f
+                                                     : __builtin_amdgcn_exp2f((big_m - cm) * p.c);
+                l *= alpha;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] *= alpha;
+                big_m = cm;
+            }
+#pragma unroll
+            for (int u = 0; u < CHUNK; ++u) {
+                if (mi[u] == kNegInf) continue;       // l and acc of such a part are ignored
+                const float w = __builtin_amdgcn_exp2f((mi[u] - big_m) * p.c);
+                l = __builtin_fmaf(w, li[u], l);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, ai[u][e], acc[e]);
             }
         }
         const float inv = l > 0.0f ? 1.0f / l : 0.0f;

@@ -21,6 +21,8 @@ Workloads (shapes, value distributions and masks):
              plus per-batch key lengths uniform in [N/2, N] as a prefix mask
   decode     B=8 H=8 N_q=1 N_k=32768 d=128 bf16 non-causal, N(0, 0.5^2): one
              new query per sequence over the long-context geometry
+  softmax    8192 score rows of 8192 fp32 entries ~ N(0, 1) (one head of the
+             headline's score matrix), for the standalone row softmax
 """
 
 import math
@@ -38,6 +40,19 @@ WORKLOADS = {
     "decode": dict(B=8, H=8, N=32768, Nq=1, d=128, dtype="bf16", causal=False, std=0.5,
                    seed=1006),
 }
+
+# Score rows for the standalone row softmax: one head's full score matrix of
+# the headline shape (8192 x 8192), whose entries q.k / sqrt(d) are N(0, 1)
+# for N(0, 1) queries and keys.
+ROW_WORKLOADS = {
+    "softmax": dict(rows=8192, n=8192, dtype="f32", std=1.0, seed=1007),
+}
+
+
+def row_workload(name):
+    w = dict(ROW_WORKLOADS[name])
+    w["s"] = gaussian((w["rows"], w["n"]), w["seed"], w["std"], w["dtype"])
+    return w
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 

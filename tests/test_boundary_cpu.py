@@ -30,8 +30,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert _declared_functions() == ["fa_fwd", "fa_fwd_ex", "fa_fwd_splitkv", "fa_merge_states",
-                                     "fa_splitkv_splits", "fa_splitkv_workspace_bytes",
-                                     "fa_strerror"]
+                                     "fa_softmax_rows", "fa_splitkv_splits",
+                                     "fa_splitkv_workspace_bytes", "fa_strerror"]
 
 
 def test_header_compiles_as_c_and_cxx(tmp_path):
@@ -153,6 +153,30 @@ def test_merge_argument_errors(lib, kw, code):
     assert _merge(**kw) == code
 
 
+def _softmax(s=FAKE, p=FAKE2, m=FAKE3, l=FAKE4, rows=10, n=100, dt=0):
+    return fa.load_library().fa_softmax_rows(s, p, m, l, rows, n, dt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(s=None), fa.FA_ERR_NULL), (dict(p=None), fa.FA_ERR_NULL), (dict(rows=0), fa.FA_ERR_SHAPE),
+    (dict(n=-1), fa.FA_ERR_SHAPE), (dict(rows=1 << 40, n=1 << 40), fa.FA_ERR_SHAPE),
+    (dict(dt=5), fa.FA_ERR_DTYPE), (dict(p=FAKE + 4), fa.FA_ERR_ALIAS),
+    (dict(m=FAKE + 40), fa.FA_ERR_ALIAS), (dict(l=FAKE2 + 8), fa.FA_ERR_ALIAS),
+    (dict(l=FAKE3 + 4), fa.FA_ERR_ALIAS),
+])
+def test_softmax_argument_errors(lib, kw, code):
+    assert _softmax(**kw) == code
+
+
+def test_softmax_valid_arguments_without_gpu(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _softmax() == fa.FA_ERR_DEVICE
+    assert _softmax(p=FAKE) == fa.FA_ERR_DEVICE            # in place
+    assert _softmax(m=None, l=None) == fa.FA_ERR_DEVICE
+
+
 def test_binding_raises_with_the_message(lib):
     with pytest.raises(fa.FaError) as e:
         fa.fa_fwd_ex(FAKE, FAKE2, FAKE3, FAKE4, FAKE5, 1, 1, 8, 8, 100, 0.125, 0, None, 1, None)
@@ -185,3 +209,5 @@ def test_every_kernel_has_its_host_stub():
     assert len(defined) >= 64, len(defined)
     merge = [l for l in out.splitlines() if "__device_stub__fa_merge_kernel<" in l]
     assert len(merge) == 4, merge
+    sm = [l for l in out.splitlines() if "__device_stub__fa_softmax_rows_kernel<" in l]
+    assert len(sm) == 4, sm
