@@ -15,8 +15,13 @@
 // one block -- and the 256 partial states (m, l) are then combined with the
 // same identity: rewrite both to the larger maximum and add.  The row is
 // HBM-bound: per entry pass 1 costs about five vector instructions and pass 2
-// four, far below what the SIMDs can issue while the row streams in; the
-// second read of a row usually hits L2.
+// four, far below what the SIMDs can issue while the row streams in.
+//
+// Rows of at most KEEP vectors per thread (8192 fp32 or 16384 bf16 entries
+// for KEEP = 8) are read from memory once: pass 1 issues all of a thread's
+// loads at once and keeps the raw vectors in registers, and pass 2 computes
+// from them.  Longer rows are read twice; the second read then mostly hits
+// L2 or the MALL.
 //
 // exp(x) is computed as exp2(x * log2 e) with x = s - m formed first: the
 // difference is exact or nearly so, and an exponent error of one rounding of
@@ -136,19 +141,102 @@ __device__ __forceinline__ void store_one(void *row, int64_t j, float y)
 
 }  // namespace
 
+// A row vector as it is kept between the passes: four floats, or eight
+// bf16 in four 32-bit words.  (Elements of an integer vector are never
+// bit-cast to float one by one: that form has been compiled to read element
+// 0 for every element.)
+template <bool BF16>
+struct RawVec {
+    typedef sf32x4 type;
+};
+template <>
+struct RawVec<true> {
+    typedef su32x4 type;
+};
+
+template <bool BF16>
+__device__ __forceinline__ void unpack(const typename RawVec<BF16>::type &u,
+                                       float (&x)[BF16 ? 8 : 4])
+{
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if constexpr (BF16) {
+            x[2 * e] = bf16_to_f32(u[e] & 0xffffu);
+            x[2 * e + 1] = bf16_to_f32(u[e] >> 16);
+        } else {
+            x[e] = u[e];
+        }
+    }
+}
+
+// The 256 per-thread states (m, l) combined into the row's, in every thread:
+// within the wave, then across the 4 waves through LDS.
+__device__ __forceinline__ void combine_workgroup(float &m, float &l, float *red_m, float *red_l)
+{
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        combine(m, l, __shfl_xor(m, off), __shfl_xor(l, off));
+    if ((tid & 63) == 0) {
+        red_m[tid >> 6] = m;
+        red_l[tid >> 6] = l;
+    }
+    __syncthreads();
+    m = red_m[0];
+    l = red_l[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) combine(m, l, red_m[i], red_l[i]);
+    __syncthreads();     // red_* is reused by the next row
+}
+
 // VEC: the rows are 16-byte aligned and a whole number of vectors long.
-template <bool BF16, bool VEC>
+// KEEP > 0 (with VEC): every row has at most KEEP * 256 vectors, held in
+// registers between the passes.
+template <bool BF16, bool VEC, int KEEP>
 __global__ __launch_bounds__(256) void fa_softmax_rows_kernel(const SoftmaxParams p)
 {
     constexpr int E = BF16 ? 8 : 4;
     constexpr int ESZ = BF16 ? 2 : 4;
     __shared__ float red_m[4], red_l[4];
     const int tid = threadIdx.x;
-    const int w = tid >> 6;
 
     for (int64_t row = blockIdx.x; row < p.rows; row += gridDim.x) {
         const void *src = static_cast<const char *>(p.s) + row * p.n * ESZ;
         void *dst = static_cast<char *>(p.p) + row * p.n * ESZ;
+
+        if (KEEP > 0) {
+            const int nv = (int)(p.n / E);
+            typedef typename RawVec<BF16>::type Raw;
+            Raw raw[KEEP > 0 ? KEEP : 1];
+#pragma unroll
+            for (int u = 0; u < KEEP; ++u)
+                if (tid + 256 * u < nv) raw[u] = reinterpret_cast<const Raw *>(src)[tid + 256 * u];
+            float m = kNegInfS, l = 0.0f;
+#pragma unroll
+            for (int u = 0; u < KEEP; ++u)
+                if (tid + 256 * u < nv) {
+                    float x[E];
+                    unpack<BF16>(raw[u], x);
+                    absorb<E>(m, l, x);
+                }
+            combine_workgroup(m, l, red_m, red_l);
+            const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+            const float base = m == kNegInfS ? 0.0f : m;
+#pragma unroll
+            for (int u = 0; u < KEEP; ++u)
+                if (tid + 256 * u < nv) {
+                    float x[E];
+                    unpack<BF16>(raw[u], x);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) x[e] = ex(x[e] - base) * inv;
+                    store_vec<BF16>(dst, tid + 256 * u, x);
+                }
+            if (tid == 0) {
+                if (p.m) p.m[row] = m;
+                if (p.l) p.l[row] = l;
+            }
+            continue;
+        }
 
         // pass 1: this thread's running state over its blocks
         float m = kNegInfS, l = 0.0f;
@@ -166,20 +254,7 @@ __global__ __launch_bounds__(256) void fa_softmax_rows_kernel(const SoftmaxParam
             }
         }
 
-        // the 256 states combined: within the wave, then across the 4 waves
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1)
-            combine(m, l, __shfl_xor(m, off), __shfl_xor(l, off));
-        if ((tid & 63) == 0) {
-            red_m[w] = m;
-            red_l[w] = l;
-        }
-        __syncthreads();
-        m = red_m[0];
-        l = red_l[0];
-#pragma unroll
-        for (int i = 1; i < 4; ++i) combine(m, l, red_m[i], red_l[i]);
-        __syncthreads();     // red_* is reused by the next row
+        combine_workgroup(m, l, red_m, red_l);
 
         // pass 2: p_j = exp(s_j - m) / l; all -inf rows give 0
         const float inv = l > 0.0f ? 1.0f / l : 0.0f;
@@ -204,11 +279,11 @@ __global__ __launch_bounds__(256) void fa_softmax_rows_kernel(const SoftmaxParam
     }
 }
 
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, int KEEP>
 static hipError_t launch_softmax_v(const SoftmaxParams &p, hipStream_t stream)
 {
     const int grid = (int)(p.rows < (1 << 20) ? p.rows : (1 << 20));
-    void (*fn)(SoftmaxParams) = fa_softmax_rows_kernel<BF16, VEC>;
+    void (*fn)(SoftmaxParams) = fa_softmax_rows_kernel<BF16, VEC, KEEP>;
     hipLaunchKernelGGL(fn, dim3(grid), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
@@ -226,9 +301,16 @@ hipError_t launch_softmax_rows(const void *s, void *p, float *m, float *l, int64
     const int esz = dtype == 1 ? 2 : 4;
     const bool vec = ((reinterpret_cast<uintptr_t>(s) | reinterpret_cast<uintptr_t>(p)) & 15) == 0 &&
                      (n * esz) % 16 == 0;
-    if (dtype == 1)
-        return vec ? launch_softmax_v<true, true>(sp, stream) : launch_softmax_v<true, false>(sp, stream);
-    return vec ? launch_softmax_v<false, true>(sp, stream) : launch_softmax_v<false, false>(sp, stream);
+    constexpr int KEEP = 8;
+    const bool keep = vec && n * esz <= (int64_t)KEEP * 256 * 16;
+    if (dtype == 1) {
+        if (keep) return launch_softmax_v<true, true, KEEP>(sp, stream);
+        return vec ? launch_softmax_v<true, true, 0>(sp, stream)
+                   : launch_softmax_v<true, false, 0>(sp, stream);
+    }
+    if (keep) return launch_softmax_v<false, true, KEEP>(sp, stream);
+    return vec ? launch_softmax_v<false, true, 0>(sp, stream)
+               : launch_softmax_v<false, false, 0>(sp, stream);
 }
 
 }  // namespace fa

@@ -4,8 +4,9 @@ The kernel runs the pages' recurrence with the values removed: one pass for
 the running (m, l), one that writes p = exp(s - m) / l ("2.2b: FlashAttention
 -- Online Softmax", "The Challenge: Computing m and l in Blocks" through "When
 Rescaling Actually Happens").  The oracle is the fp64 three-pass safe softmax
-of each row (oracle.softmax_row).  Rows cover the pages' toy row, every length
-class of the kernel (16-byte vectors, unaligned rows, short rows), masked
+of each row (oracle.softmax_row).  Rows cover the pages' toy row, every path of
+the kernel (rows held in registers between the passes, longer rows read
+twice, unaligned rows, short rows), masked
 (-inf) entries, fully masked rows, scores far beyond exp's range, and
 in-place use.
 """
@@ -87,7 +88,7 @@ def test_pages_toy_row(dt):
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("rows,n", [(1, 1), (3, 5), (7, 1000), (64, 1001), (33, 8192),
-                                    (5, 100003), (300, 64)])
+                                    (5, 100003), (300, 64), (4, 40000)])
 @pytest.mark.parametrize("sigma", [1.0, 30.0])
 def test_random_rows(dt, rows, n, sigma):
     g = torch.Generator().manual_seed(3000 + rows + n)
