@@ -128,6 +128,44 @@ def cpu_baseline(w, seconds):
     }
 
 
+def cpu_tiled(w, seconds):
+    """The host-CPU tiled implementation of the same recurrence
+    (libfa_cpu.so) on whole heads of the workload, as many as fit in about
+    `seconds`, on every core this process may use; in the metric's unit."""
+    import numpy as np
+    import torch
+    from online_softmax_fa_amd import cpu
+
+    B, H, N, d, Nq = w["B"], w["H"], w["N"], w["d"], w["Nq"]
+    bf16 = w["dtype"] == "bf16"
+    threads = len(os.sched_getaffinity(0))
+
+    def arr(t, nh):
+        x = t.reshape(B * H, -1, d)[:nh].contiguous()
+        return x.view(torch.int16).numpy().view(np.uint16) if bf16 else x.numpy()
+
+    def timed(nh):
+        q, k, v = (arr(w[x], nh).reshape(1, nh, -1, d) for x in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        _, _, used = cpu.attention_cpu(q, k, v, w["scale"], w["causal"], None, threads,
+                                       dtype="bf16" if bf16 else "f32")
+        return time.perf_counter() - t0, used
+
+    nh = 1
+    dt, used = timed(nh)
+    if dt < seconds and nh < B * H:
+        nh = int(min(B * H, max(1, seconds / max(dt, 1e-3))))
+        dt, used = timed(nh)
+    esz = 2 if bf16 else 4
+    if w.get("bound") == "hbm":
+        value, unit = nh * algorithmic_bytes(1, 1, Nq, N, d, esz) / dt / 1e9, "GB/s"
+    else:
+        value, unit = nh * attention_flops(1, 1, Nq, N, d, w["causal"]) / dt / 1e12, "TFLOP/s"
+    return {"value": value, "unit": unit, "cores": int(used), "kind": "cpu_tiled",
+            "sample": "%d of %d heads, libfa_cpu.so (the same recurrence, cache-tiled and "
+                      "vectorized on the host), %.1f s wall" % (nh, B * H, dt)}
+
+
 def softmax_cpu_baseline(s, seconds):
     """The fp64 oracle's three-pass softmax on evenly spaced rows, one core
     (the oracle's row entry point is single-threaded), in GB/s of the rows'
@@ -341,6 +379,9 @@ def main():
         log("timing the CPU oracle on a sample of rows ...")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
         log("cpu baseline: %s" % result["cpu_baseline"])
+        log("timing the host-CPU tiled implementation on whole heads ...")
+        result["cpu_tiled"] = cpu_tiled(w, args.cpu_seconds / 3)
+        log("cpu tiled: %s" % result["cpu_tiled"])
     print(json.dumps(result), flush=True)
 
 

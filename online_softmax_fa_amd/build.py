@@ -69,5 +69,25 @@ def build(verbose=False):
     return OUT
 
 
+CPU_SOURCE = os.path.join(_HERE, "csrc", "fa_cpu.cpp")
+CPU_OUT = os.path.join(_HERE, "libfa_cpu.so")
+
+
+def build_cpu(verbose=False):
+    """Compile libfa_cpu.so, the host-CPU implementation, with g++ (OpenMP;
+    no fast-math: the kernel relies on IEEE -inf and rounding)."""
+    tmp = CPU_OUT + ".tmp%d" % os.getpid()
+    cmd = ["g++", "-O3", "-std=c++17", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-I", os.path.join(_ROOT, "include"), CPU_SOURCE, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("g++ failed (%d):\n%s" % (r.returncode, r.stderr))
+    os.replace(tmp, CPU_OUT)
+    return CPU_OUT
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_cpu(verbose=True))
