@@ -49,9 +49,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
+# Sources that decide the HBM traffic of each workload's kernels: a stored
+# counter summary is used only while these files are unchanged.
+TRAFFIC_SOURCES = {
+    "softmax": ("fa_softmax.hip", "fa_api.cpp", "fa_internal.h"),
+}
+DEFAULT_TRAFFIC_SOURCES = ("fa_kernels.hip", "fa_api.cpp", "fa_internal.h")
+
+
+def kernel_source_hash(workload):
     h = hashlib.sha256()
-    for f in ("fa_kernels.hip", "fa_softmax.hip", "fa_api.cpp", "fa_internal.h"):
+    for f in TRAFFIC_SOURCES.get(workload, DEFAULT_TRAFFIC_SOURCES):
         with open(os.path.join(ROOT, "online_softmax_fa_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -75,7 +83,7 @@ def traffic_from_profile(workload):
         return None
     with open(path) as fh:
         t = json.load(fh)
-    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+    if t.get("kernel_source_sha256_16") != kernel_source_hash(workload):
         return None
     return t.get("bytes_per_launch")
 
