@@ -137,7 +137,8 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  *               a tile's scores exceed it by more than 16 / (scale * log2 e),
  *               so running max - that bound <= m <= running max.  Tiles the
  *               kernel never visits (above the causal diagonal of the row's
- *               query tile) leave their entries untouched.
+ *               query tile, fa_query_tile_rows rows) leave their entries
+ *               untouched.
  *   trace_b, trace_h, trace_row
  *               the traced row: batch, head and query index, each in range
  *               (else FA_ERR_ARG).  Ignored when trace is NULL.
@@ -155,6 +156,18 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
               int B, int H, int N_q, int N_k, int d, float scale, int causal,
               const uint8_t *kv_len_mask, int dtype, void *stream,
               const fa_opts *opts);
+
+/*
+ * fa_query_tile_rows -- query rows one workgroup of fa_fwd / fa_fwd_ex
+ * processes for these arguments (block_n as in fa_opts, 0 = library choice):
+ * the rows that share each key/value tile staged in on-chip memory, since
+ * query rows are independent ("2.2b", "Scaling to Multiple Queries").  Under
+ * causality a workgroup visits the key tiles up to the diagonal of the last
+ * row of its query tile, so a trace has one entry per such tile.  Returns a
+ * positive row count, or FA_ERR_HEAD_DIM / FA_ERR_DTYPE / FA_ERR_TILE.
+ * Pure function of its arguments: no device call.
+ */
+int fa_query_tile_rows(int dtype, int d, int block_n);
 
 /*
  * Split-key forward pass and the merge of partial states.

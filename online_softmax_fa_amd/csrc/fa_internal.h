@@ -38,6 +38,10 @@ struct Params {
     int trace_row;        // its query index
 };
 
+// Query rows per workgroup of the forward kernel for validated arguments
+// (dtype 0 = fp32, 1 = bf16; block_n 16, 32, 64 or 128).
+int query_tile_rows(int dtype, int block_n);
+
 // Enqueues the forward kernel for validated arguments.  dtype: 0 = fp32,
 // 1 = bf16; d: 64 or 128; block_n: 16, 32, 64 or 128.
 hipError_t launch_fwd(const Params &p, int dtype, int d, int block_n, int causal, int B, int H,

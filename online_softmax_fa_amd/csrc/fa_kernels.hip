@@ -223,7 +223,7 @@ __device__ __forceinline__ bool lazy_step(f32x16 (&s)[NKB], bf16x8 (&pb)[NT16], 
 // ---------------------------------------------------------------------------
 // bf16 kernel
 // ---------------------------------------------------------------------------
-// LDS layout of one pipeline stage: the K tile, then the V tile, each
+// LDS layout: the K tiles of the pipeline stages, then their V tiles, each
 // BNA rows of D bf16 (D*2 bytes, unpadded), both in [key][dim] order.  Tiles
 // are filled by LDS DMA (global_load_lds_dwordx4): one wave instruction
 // writes 1 KiB of contiguous LDS, so rows cannot be padded; instead the
@@ -246,6 +246,12 @@ __device__ __forceinline__ int swz_v(int r)
     return 2 * (r & 3);
 }
 
+// Waves per workgroup of the bf16 kernel: 8 (two per SIMD, one workgroup per
+// CU), so that each K/V tile staged in LDS serves 256 query rows; 4 for
+// 128-key tiles, whose score registers do not fit the 256 VGPRs a wave
+// may use when two share a SIMD.
+constexpr int bf16_waves(int bn) { return bn == 128 ? 4 : 8; }
+
 template <int D, int BN, int NW>
 struct Bf16Cfg {
     static constexpr int BM = 32 * NW;
@@ -256,12 +262,34 @@ struct Bf16Cfg {
     static constexpr int CH = ROW / 16;                  // 16-byte chunks per row
     static constexpr int TILE = BNA * ROW;               // bytes of one K or V tile
     static constexpr int STAGE = 2 * TILE;
-    static constexpr size_t LDS_BYTES = 2 * STAGE;
     static constexpr int ROWS_PER_DMA = 1024 / ROW;
     static constexpr int DMA_PER_TILE = BN * ROW / 1024;  // wave instructions per matrix
     static constexpr int DMA_PER_WAVE = (DMA_PER_TILE + NW - 1) / NW;
     static constexpr int T = NW * 64;
+    // Two pipeline stages: one tile in flight while the other is read.  (A
+    // third stage, two tiles in flight, measured slower on MI355X.)
+    static constexpr int STAGES = 2;
+    static constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE;
+    // LDS layout: the K tiles of all stages, then the V tiles.  Reads add a
+    // stage offset of at most (STAGES-1) * TILE to per-lane base addresses
+    // (the V base included in them), which stays within the 16-bit offset
+    // field of the LDS instructions.
+    static constexpr int V_BASE = STAGES * TILE;
 };
+
+// LDS DMA of 16 bytes per lane, global base + voff (bytes, per lane) to LDS
+// lds_addr + 16 * lane (global_load_lds_dwordx4; M0 holds the LDS address).
+// Written as inline assembly on purpose: the compiler then does not treat the
+// transfer as a store to LDS, and does not make every later LDS read wait for
+// all DMA in flight.  The kernel orders the two itself: a stage is read only
+// after the s_waitcnt vmcnt(0) and barrier that end the iteration filling it,
+// and refilled only after the barrier that ends the iteration reading it.
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds_addr)
+{
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(base), "{m0}"(lds_addr));
+}
 
 // s_waitcnt vmcnt(0): every vector-memory operation of this wave, LDS DMA
 // included, has completed (expcnt and lgkmcnt fields left at their maximum).
@@ -307,7 +335,7 @@ struct Bf16Fwd {
     float mc, l_part;   // exponent base fl(m_ref * c) (log2 units), this lane's share of l
     f32x16 o[D / 32];
     uint64_t kv_lo, kv_hi;
-    int mnext0, mnext1;
+    int mnext0, mnext1;     // key-padding bytes of the next tile
 
     __device__ __forceinline__ void init(const Params &p, lds_char *lds_base)
     {
@@ -381,7 +409,7 @@ struct Bf16Fwd {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
             const int e = 8 * db + 4 * (g & 1) + (i & 3);   // 8-byte chunk of the row
-            offv[db] = lbase + C::TILE + vrow * C::ROW + 16 * ((e >> 1) ^ swz_v<D>(vrow)) +
+            offv[db] = lbase + C::V_BASE + vrow * C::ROW + 16 * ((e >> 1) ^ swz_v<D>(vrow)) +
                        8 * (e & 1);
         }
 
@@ -433,18 +461,16 @@ struct Bf16Fwd {
                         ov -= over * D;
                     }
                 }
-                lds_char *dst = lds + st * C::STAGE + j * 1024;
-                __builtin_amdgcn_global_load_lds(kt + ok,
-                                                 (__attribute__((address_space(3))) void *)dst,
-                                                 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(
-                    vt + ov, (__attribute__((address_space(3))) void *)(dst + C::TILE), 16, 0, 0);
+                const uint32_t dst = (uint32_t)(uintptr_t)(lds + st * C::TILE + j * 1024);
+                dma16(kt, 2u * (uint32_t)ok, dst);
+                dma16(vt, 2u * (uint32_t)ov, dst + C::V_BASE);
             }
         }
     }
 
     // One key-padding byte per lane for tile t (two for 128-key tiles),
-    // loaded a tile ahead and turned into bits after the next wait.
+    // loaded with the tile's transfers and turned into bits after the wait
+    // for them.
     __device__ __forceinline__ void load_mask(int t)
     {
         const int j0 = t * BN + lane;
@@ -458,24 +484,38 @@ struct Bf16Fwd {
         kv_hi = __ballot(mnext1 != 0);
     }
 
-    // One iteration: prefetch tile it+1 into the other stage, compute tile it
-    // from stage ST, then wait for the prefetch and synchronise.
     // Key tile visited at step it.
     __device__ __forceinline__ int tile_at(int it) const
     {
         return t_lo + (reverse ? (n_t - 1 - it) : it);
     }
 
+    // Transfers of the tile visited at step it, into stage `st`.
+    __device__ __forceinline__ void fetch(int it, int st)
+    {
+        const int t = tile_at(it);
+        if (Mg) load_mask(t);
+        issue_tile(t, st);
+    }
+
+    // Wait until every transfer of this wave has landed, then synchronise:
+    // after it the tile fetched last is readable by all waves, and the stage
+    // read before it is free to be refilled.
+    __device__ __forceinline__ void land()
+    {
+        wait_vmem();
+        __syncthreads();
+    }
+
+    // One iteration: start the transfers of step it + 1 into the other
+    // stage, compute step it from stage ST, then wait for step it + 1's tile
+    // and synchronise.
     template <int ST>
     __device__ __forceinline__ void iteration(int it)
     {
         const int t = tile_at(it);
         const bool has_next = it + 1 < n_t;
-        if (has_next) {
-            const int tn = tile_at(it + 1);
-            if (Mg) load_mask(tn);
-            issue_tile(tn, ST ^ 1);
-        }
+        if (has_next) fetch(it + 1, ST ^ 1);
 
         const int k0 = t * BN;
         const bool tile_empty = Mg && kv_lo == 0 && (BN <= 64 || kv_hi == 0);
@@ -485,9 +525,10 @@ struct Bf16Fwd {
         if (!wave_skip) compute<ST>(k0);
         if (TRACE && trace_on) record(it, t);
 
-        wait_vmem();
-        __syncthreads();
-        if (Mg && has_next) take_mask();
+        if (has_next) {
+            land();
+            if (Mg) take_mask();
+        }
     }
 
     // Raw scores S^T = K . Q^T of the tile in stage ST ("The math of
@@ -504,7 +545,7 @@ struct Bf16Fwd {
         for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb)
-                kfr[kk][kb] = *(const lds_bf16x8 *)(uintptr_t)(offk[kk] + ST * C::STAGE +
+                kfr[kk][kb] = *(const lds_bf16x8 *)(uintptr_t)(offk[kk] + ST * C::TILE +
                                                                 kb * 32 * C::ROW);
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
@@ -554,12 +595,39 @@ struct Bf16Fwd {
         }
     }
 
+    // V operand of P.V product i (k-step i / (D/32), dims 32*(i % (D/32)) ..
+    // +31) from the tile in stage ST, through two transposing reads: within
+    // a group of 16 lanes, lane j receives element j%4 of the 8-byte chunks
+    // addressed by lanes 4m + j/4, so the operand holds exactly the keys the
+    // score layout gives this lane's weights.
+    template <int ST>
+    __device__ __forceinline__ bf16x8 load_v(int i) const
+    {
+        const int t16 = i / (D / 32), db = i % (D / 32);
+        const uint32_t row = offv[db] + ST * C::TILE + 16 * t16 * C::ROW;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)row);
+        const s16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)(row + 8 * C::ROW));
+        const s16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8, av);
+    }
+
     template <int ST>
     __device__ __forceinline__ void compute(int k0)
     {
         f32x16 s[C::NKB];
         qk<ST>(s);
         mask_scores(k0, s);
+        // The V operands of the first VA products are read now, so that the
+        // softmax below hides their LDS latency; the product loop then keeps
+        // VA products' operands in flight.
+        constexpr int NPV = C::NT16 * (D / 32);
+        constexpr int VA_MAX = C::NKB >= 4 ? 2 : 4;        // fewer where the scores take more registers
+        constexpr int VA = NPV < VA_MAX ? NPV : VA_MAX;
+        bf16x8 vf[NPV];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < VA; ++i) vf[i] = load_v<ST>(i);
         bf16x8 pb[C::NT16];
         // Fast path: the weights against the current base, without the tile
         // maximum.  They are kept when every lane's sum of them is at most
@@ -578,6 +646,9 @@ struct Bf16Fwd {
             }
         const float tot = (fs[0] + fs[1]) + (fs[2] + fs[3]);
         const bool done = !__any(!(tot <= 65536.0f));
+        // the V reads first, then the vector work
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * VA, 9);
+        __builtin_amdgcn_sched_group_barrier(0x406, 512, 9);
         if (done) {
 #pragma unroll
             for (int t16 = 0; t16 < C::NT16; ++t16)
@@ -600,17 +671,15 @@ struct Bf16Fwd {
         // +15; this lane's 8 weights are registers 8*(t16%2) .. +7 of key
         // block t16/2, i.e. keys 16*t16 + 4h + {0..3, 8..11}.
 #pragma unroll
-        for (int t16 = 0; t16 < C::NT16; ++t16) {
+        for (int i = 0; i < NPV; ++i) {
+            if (i + VA < NPV) vf[i + VA] = load_v<ST>(i + VA);
+            const int t16 = i / (D / 32), db = i % (D / 32);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pb[t16], o[db], 0, 0, 0);
+        }
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const uint32_t row = offv[db] + ST * C::STAGE + 16 * t16 * C::ROW;
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)row);
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4 *)(uintptr_t)(row + 8 * C::ROW));
-                const s16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
-                                                                pb[t16], o[db], 0, 0, 0);
-            }
+        for (int i = 0; i < NPV; ++i) {
+            if (i + VA < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 6);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 6);
         }
     }
 
@@ -681,29 +750,25 @@ struct Bf16Fwd {
 // Workgroups per CU the kernel is compiled for: two waves per SIMD (at most
 // 256 VGPRs per lane) when the LDS of that many workgroups fits, else one
 // workgroup.
-constexpr int bf16_blocks_per_cu(int d, int bn, int nw)
+template <int D, int BN, int NW>
+constexpr int bf16_blocks_per_cu()
 {
-    const int by_waves = 8 / nw;
-    const int by_lds = 2 * 2 * (bn < 32 ? 32 : bn) * d * 2 <= 81920 ? 2 : 1;
+    const int by_waves = 8 / NW;
+    const int by_lds = 2 * Bf16Cfg<D, BN, NW>::LDS_BYTES <= 160 * 1024 ? 2 : 1;
     const int b = by_waves < by_lds ? by_waves : by_lds;
     return b < 1 ? 1 : b;
 }
 
 template <int D, int BN, int NW, bool CAUSAL, bool TRACE>
-__global__ __launch_bounds__(NW * 64, bf16_blocks_per_cu(D, BN, NW)) void fa_fwd_bf16_kernel(
+__global__ __launch_bounds__(NW * 64, (bf16_blocks_per_cu<D, BN, NW>())) void fa_fwd_bf16_kernel(
     const Params p)
 {
     extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
     Bf16Fwd<D, BN, NW, CAUSAL, TRACE> k;
     k.init(p, (lds_char *)lds_raw);
 
-    if (k.n_t > 0) {
-        const int t0 = k.tile_at(0);
-        if (k.Mg) k.load_mask(t0);
-        k.issue_tile(t0, 0);
-    }
-    wait_vmem();
-    __syncthreads();
+    if (k.n_t > 0) k.fetch(0, 0);
+    k.land();
     if (k.Mg) k.take_mask();
 
     for (int it = 0; it < k.n_t; it += 2) {
@@ -1026,7 +1091,7 @@ static hipError_t launch_variant(int causal, int grid, int threads, size_t lds,
 template <int D, int BN>
 static hipError_t dispatch_bf16(const Params &p0, int causal, int B, int H, hipStream_t stream)
 {
-    constexpr int NW = 4;
+    constexpr int NW = bf16_waves(BN);
     using C = Bf16Cfg<D, BN, NW>;
     Params p = p0;
     p.n_qt = (p.Nq + C::BM - 1) / C::BM;
@@ -1063,6 +1128,11 @@ static hipError_t dispatch_d(const Params &p, int dtype, int block_n, int causal
     case 128: return dispatch_f32<D, 128>(p, causal, B, H, s);
     default: return dispatch_f32<D, 64>(p, causal, B, H, s);
     }
+}
+
+int query_tile_rows(int dtype, int block_n)
+{
+    return dtype == 1 ? 32 * bf16_waves(block_n) : 32 * 4;
 }
 
 hipError_t launch_fwd(const Params &p, int dtype, int d, int block_n, int causal, int B, int H,

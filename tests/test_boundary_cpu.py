@@ -30,8 +30,22 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert _declared_functions() == ["fa_fwd", "fa_fwd_ex", "fa_fwd_splitkv", "fa_merge_states",
-                                     "fa_softmax_rows", "fa_splitkv_splits",
+                                     "fa_query_tile_rows", "fa_softmax_rows", "fa_splitkv_splits",
                                      "fa_splitkv_workspace_bytes", "fa_strerror"]
+
+
+def test_query_tile_rows(lib):
+    """Rows per workgroup: a whole number of 32-row wave tiles, fixed by the
+    arguments alone (no device needed); bad arguments give their status."""
+    for dtype in (fa.FA_DTYPE_F32, fa.FA_DTYPE_BF16):
+        for d in (64, 128):
+            for bn in (0, 16, 32, 64, 128):
+                r = lib.fa_query_tile_rows(dtype, d, bn)
+                assert r > 0 and r % 32 == 0
+            assert lib.fa_query_tile_rows(dtype, d, 0) == lib.fa_query_tile_rows(dtype, d, 64)
+    assert lib.fa_query_tile_rows(fa.FA_DTYPE_BF16, 96, 64) == fa.FA_ERR_HEAD_DIM
+    assert lib.fa_query_tile_rows(7, 64, 64) == fa.FA_ERR_DTYPE
+    assert lib.fa_query_tile_rows(fa.FA_DTYPE_BF16, 64, 48) == fa.FA_ERR_TILE
 
 
 def test_header_compiles_as_c_and_cxx(tmp_path):
