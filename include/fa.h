@@ -164,10 +164,11 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
  * query rows are independent ("2.2b", "Scaling to Multiple Queries").  Under
  * causality a workgroup visits the key tiles up to the diagonal of the last
  * row of its query tile, so a trace has one entry per such tile.  Returns a
- * positive row count, or FA_ERR_HEAD_DIM / FA_ERR_DTYPE / FA_ERR_TILE.
- * Pure function of its arguments: no device call.
+ * positive row count, or FA_ERR_SHAPE (N_q < 1) / FA_ERR_HEAD_DIM /
+ * FA_ERR_DTYPE / FA_ERR_TILE.  Pure function of its arguments: no device
+ * call.
  */
-int fa_query_tile_rows(int dtype, int d, int block_n);
+int fa_query_tile_rows(int dtype, int d, int N_q, int block_n);
 
 /*
  * Split-key forward pass and the merge of partial states.

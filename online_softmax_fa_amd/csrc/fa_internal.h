@@ -39,8 +39,8 @@ struct Params {
 };
 
 // Query rows per workgroup of the forward kernel for validated arguments
-// (dtype 0 = fp32, 1 = bf16; block_n 16, 32, 64 or 128).
-int query_tile_rows(int dtype, int block_n);
+// (dtype 0 = fp32, 1 = bf16; block_n 16, 32, 64 or 128; n_q >= 1).
+int query_tile_rows(int dtype, int block_n, int n_q);
 
 // Enqueues the forward kernel for validated arguments.  dtype: 0 = fp32,
 // 1 = bf16; d: 64 or 128; block_n: 16, 32, 64 or 128.

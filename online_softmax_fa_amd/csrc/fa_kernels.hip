@@ -249,8 +249,10 @@ __device__ __forceinline__ int swz_v(int r)
 // Waves per workgroup of the bf16 kernel: 8 (two per SIMD, one workgroup per
 // CU), so that each K/V tile staged in LDS serves 256 query rows; 4 for
 // 128-key tiles, whose score registers do not fit the 256 VGPRs a wave
-// may use when two share a SIMD.
-constexpr int bf16_waves(int bn) { return bn == 128 ? 4 : 8; }
+// may use when two share a SIMD, and for at most 128 query rows, which
+// cannot occupy 8 waves: there two 4-wave workgroups per CU keep twice the
+// K/V transfers in flight (decoding is bound by reading K and V).
+constexpr int bf16_waves(int bn, int nq) { return bn == 128 || nq <= 128 ? 4 : 8; }
 
 template <int D, int BN, int NW>
 struct Bf16Cfg {
@@ -1088,15 +1090,25 @@ static hipError_t launch_variant(int causal, int grid, int threads, size_t lds,
                  : launch_instance<D, BN, NW, false, false, BF16>(grid, threads, lds, stream, p);
 }
 
-template <int D, int BN>
-static hipError_t dispatch_bf16(const Params &p0, int causal, int B, int H, hipStream_t stream)
+template <int D, int BN, int NW>
+static hipError_t dispatch_bf16_nw(const Params &p0, int causal, int B, int H, hipStream_t stream)
 {
-    constexpr int NW = bf16_waves(BN);
     using C = Bf16Cfg<D, BN, NW>;
     Params p = p0;
     p.n_qt = (p.Nq + C::BM - 1) / C::BM;
     const int grid = B * H * p.n_qt * p.n_split;
     return launch_variant<D, BN, NW, true>(causal, grid, C::T, C::LDS_BYTES, stream, p);
+}
+
+template <int D, int BN>
+static hipError_t dispatch_bf16(const Params &p, int causal, int B, int H, hipStream_t stream)
+{
+    if constexpr (BN == 128)
+        return dispatch_bf16_nw<D, BN, 4>(p, causal, B, H, stream);
+    else if (bf16_waves(BN, p.Nq) == 4)
+        return dispatch_bf16_nw<D, BN, 4>(p, causal, B, H, stream);
+    else
+        return dispatch_bf16_nw<D, BN, 8>(p, causal, B, H, stream);
 }
 
 template <int D, int BN>
@@ -1130,9 +1142,9 @@ static hipError_t dispatch_d(const Params &p, int dtype, int block_n, int causal
     }
 }
 
-int query_tile_rows(int dtype, int block_n)
+int query_tile_rows(int dtype, int block_n, int n_q)
 {
-    return dtype == 1 ? 32 * bf16_waves(block_n) : 32 * 4;
+    return dtype == 1 ? 32 * bf16_waves(block_n, n_q) : 32 * 4;
 }
 
 hipError_t launch_fwd(const Params &p, int dtype, int d, int block_n, int causal, int B, int H,

@@ -39,13 +39,16 @@ def test_query_tile_rows(lib):
     arguments alone (no device needed); bad arguments give their status."""
     for dtype in (fa.FA_DTYPE_F32, fa.FA_DTYPE_BF16):
         for d in (64, 128):
-            for bn in (0, 16, 32, 64, 128):
-                r = lib.fa_query_tile_rows(dtype, d, bn)
-                assert r > 0 and r % 32 == 0
-            assert lib.fa_query_tile_rows(dtype, d, 0) == lib.fa_query_tile_rows(dtype, d, 64)
-    assert lib.fa_query_tile_rows(fa.FA_DTYPE_BF16, 96, 64) == fa.FA_ERR_HEAD_DIM
-    assert lib.fa_query_tile_rows(7, 64, 64) == fa.FA_ERR_DTYPE
-    assert lib.fa_query_tile_rows(fa.FA_DTYPE_BF16, 64, 48) == fa.FA_ERR_TILE
+            for nq in (1, 128, 129, 8192):
+                for bn in (0, 16, 32, 64, 128):
+                    r = lib.fa_query_tile_rows(dtype, d, nq, bn)
+                    assert r > 0 and r % 32 == 0
+                assert (lib.fa_query_tile_rows(dtype, d, nq, 0) ==
+                        lib.fa_query_tile_rows(dtype, d, nq, 64))
+    assert lib.fa_query_tile_rows(fa.FA_DTYPE_BF16, 64, 0, 64) == fa.FA_ERR_SHAPE
+    assert lib.fa_query_tile_rows(fa.FA_DTYPE_BF16, 96, 8, 64) == fa.FA_ERR_HEAD_DIM
+    assert lib.fa_query_tile_rows(7, 64, 8, 64) == fa.FA_ERR_DTYPE
+    assert lib.fa_query_tile_rows(fa.FA_DTYPE_BF16, 64, 8, 48) == fa.FA_ERR_TILE
 
 
 def test_header_compiles_as_c_and_cxx(tmp_path):

@@ -195,7 +195,9 @@ def test_edge_shapes(dtype, shape):
         mask[0, : min(5, Nk)] = 0
     scale = inputs.default_scale(d)
     o_ref, lse_ref = run_oracle(q, k, v, scale, causal=causal, mask=mask)
-    for bn in (16, 64, 128):
+    # every tile size, each reached with both workgroup shapes (query tiles
+    # of 128 rows for N_q <= 128, 256 rows above; see fa_query_tile_rows)
+    for bn in (16, 32, 64, 128):
         say("edge %s %s bn=%d" % (dtype, shape, bn))
         o, lse = run_gpu(q, k, v, scale, causal=causal, mask=mask, block_n=bn)
         compare(o, lse, o_ref, lse_ref, dtype, what="bn%d" % bn)
