@@ -54,7 +54,7 @@ def log(*a):
 TRAFFIC_SOURCES = {
     "softmax": ("fa_softmax.hip", "fa_api.cpp", "fa_internal.h"),
 }
-DEFAULT_TRAFFIC_SOURCES = ("fa_kernels.hip", "fa_api.cpp", "fa_internal.h")
+DEFAULT_TRAFFIC_SOURCES = ("fa_kernels.hip", "fa_device.h", "fa_api.cpp", "fa_internal.h")
 
 
 def kernel_source_hash(workload):

@@ -1,0 +1,209 @@
+// fa_device.h -- device-side helpers shared by the kernel files of
+// libfa.so: vector types, the MFMA register layout, cross-lane reductions,
+// LDS swizzles, LDS DMA and the launch helper.  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "fa_internal.h"
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+static constexpr float kNegInf = -__builtin_inff();
+static constexpr float kLn2 = 0.693147180559945309f;
+
+// ---------------------------------------------------------------------------
+// Grid mapping.  Workgroups are dispatched round-robin over the 8 XCDs
+// (workgroup g runs on XCD g % 8).  The logical index gives every XCD a
+// contiguous range of work items, ordered head by head, so the query tiles of
+// one (batch, head) run together on one XCD and share its L2 for K and V.
+// Within a head, causal query tiles go longest first.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int logical_tile(int g, int G)
+{
+    const int per = G >> 3, rem = G & 7;
+    const int x = g & 7, j = g >> 3;
+    return x * per + (x < rem ? x : rem) + j;
+}
+
+// Position, inside a 32-key block, of register r of a lane with half h = l/32:
+// key = 8*(r/4) + 4*h + r%4.  kpos(r) is the part that does not depend on h.
+__device__ __forceinline__ constexpr int kpos(int r) { return 8 * (r >> 2) + (r & 3); }
+
+// Visibility bits of the 32 keys of one key block, as seen by this lane: bit
+// kpos(r) set <=> register r holds a visible key.
+//   lim      number of leading keys (from the lane's first key) inside both
+//            the causal limit and N_k, clamped to [0, 32]
+//   kvbits   key-padding bits of the block, already shifted by 4*h
+__device__ __forceinline__ uint32_t prefix_bits(int lim)
+{
+    return lim >= 32 ? 0xffffffffu : (lim <= 0 ? 0u : ((1u << lim) - 1u));
+}
+
+template <int NKB>
+__device__ __forceinline__ void apply_visibility(f32x16 (&s)[NKB], const uint32_t (&vis)[NKB])
+{
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            s[kb][r] = ((vis[kb] >> kpos(r)) & 1u) ? s[kb][r] : kNegInf;
+}
+
+// Value of x in the lane l ^ 32 combined with x by `op`, in every lane: one
+// v_permlane32_swap exchanges the two 32-lane halves, and both operands of
+// the combination are the same two values in every lane (so both halves get
+// bitwise the same result).
+__device__ __forceinline__ float pair_max(float x)
+{
+    const int xi = __builtin_bit_cast(int, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+    return fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x)
+{
+    const int xi = __builtin_bit_cast(int, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+    return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+}
+
+// The recurrence step of the bf16 kernels, with a lagging reference, over
+// NKB blocks of 32 keys (16 scores per lane each).
+//
+// The exponent base mc = fl(m_ref * c) (log2 units) follows the running
+// maximum, but moves only when a step's maximum exceeds it by more than
+// kLag.  Until then the weights exp2(s*c - mc) may exceed 1, up to
+// 2^kLag = 256 here and 2^16 on the kernels' fast path that skips this step
+// -- far from any fp32 or bf16 limit -- and alpha is exactly 1,
+// so the rescale of o~ is skipped; when the base does move,
+// alpha = exp2(mc_old - mc_new) < 2^-kLag rescales l and o~ as the pages'
+// recurrence does.  l and o~ are always stated against the same base, so
+// o~ / l and lse = (mc + log2 l) ln 2 are the same quantities as with the
+// exact running maximum ("2.2b", "Why This Algorithm is Exact": any common
+// reference cancels; "The math of FlashAttention", "Proof of numerical
+// stability": here every exponent is at most 16 instead of 0).
+//
+// s: raw scores in (hidden keys at -inf), fp32 weights out; l_part: this
+// lane's share of l, summed over the fp32 weights.  Returns whether o~ must
+// be rescaled by `alpha`: some row of the wave moved its base after having
+// seen a visible key.  While every key so far is hidden mc stays -inf and
+// the weights are exp2(-inf) = 0.
+static constexpr float kLag = 8.0f;
+
+template <int NKB>
+__device__ __forceinline__ bool lazy_step(f32x16 (&s)[NKB], float &mc, float &l_part, float c,
+                                          float &alpha)
+{
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = pair_max(mx);
+    const float mxc = mx * c;                       // -inf when the step is all hidden
+    const bool grow = mxc > mc + kLag;              // always true on the first visible step
+    const float mc_new = grow ? mxc : mc;
+    alpha = grow ? __builtin_amdgcn_exp2f(mc - mc_new) : 1.0f;
+    const bool rescale = __any(grow && mc != kNegInf);
+    mc = mc_new;
+    const float base = (mc_new == kNegInf) ? 0.0f : mc_new;
+
+    // l sums the fp32 weights (before they are rounded for the product), so
+    // lse keeps fp32 accuracy; four partial sums keep the adds independent.
+    float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -base));
+            s[kb][r] = pv;
+            sum[r & 3] += pv;
+        }
+    l_part = l_part * alpha + ((sum[0] + sum[1]) + (sum[2] + sum[3]));
+    return rescale;
+}
+
+// LDS tiles of the bf16 kernels: BN rows of D bf16 (D*2 bytes, unpadded), K
+// and V both in [key][dim] order.  Tiles
+// are filled by LDS DMA (global_load_lds_dwordx4): one wave instruction
+// writes 1 KiB of contiguous LDS, so rows cannot be padded; instead the
+// 16-byte chunks of each row are XOR-permuted (swz_k, swz_v) and every lane
+// loads the global chunk that belongs at its LDS slot.  The permutations keep
+// the two LDS read patterns free of bank conflicts:
+//   K (ds_read_b128): 32 consecutive rows, one 16-byte chunk each;
+//   V (ds_read_b64_tr_b16): per half wave, 4 consecutive rows x 64 bytes.
+template <int D>
+__device__ __forceinline__ int swz_k(int r)
+{
+    if (D == 128) return r & 15;
+    return ((r >> 1) & 7) ^ ((r & 1) << 2);
+}
+
+template <int D>
+__device__ __forceinline__ int swz_v(int r)
+{
+    if (D == 128) return (0xAC60 >> (4 * (r & 3))) & 15;   // 0, 6, 12, 10
+    return 2 * (r & 3);
+}
+
+// LDS DMA of 16 bytes per lane, global base + voff (bytes, per lane) to LDS
+// lds_addr + 16 * lane (global_load_lds_dwordx4; M0 holds the LDS address).
+// Written as inline assembly on purpose: the compiler then does not treat the
+// transfer as a store to LDS, and does not make every later LDS read wait for
+// all DMA in flight.  The kernel orders the two itself: a stage is read only
+// after the s_waitcnt vmcnt(0) and barrier that end the iteration filling it,
+// and refilled only after the barrier that ends the iteration reading it.
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds_addr)
+{
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(base), "{m0}"(lds_addr));
+}
+
+// s_waitcnt vmcnt(0): every vector-memory operation of this wave, LDS DMA
+// included, has completed (expcnt and lgkmcnt fields left at their maximum).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int N>
+struct IntC {
+    static constexpr int value = N;
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+
+// ---------------------------------------------------------------------------
+// Launch helper
+// ---------------------------------------------------------------------------
+// Dynamic LDS above the default limit is opted into once per kernel and
+// device; `done` is the per-kernel record of devices already set up.
+inline hipError_t launch(const void *kernel, void (*fn)(Params), std::atomic<uint64_t> &done,
+                         int grid, int threads, size_t lds, hipStream_t stream, const Params &p)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = 1ull << (dev & 63);
+    if (!(done.load(std::memory_order_acquire) & bit)) {
+        e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        done.fetch_or(bit, std::memory_order_acq_rel);
+    }
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(threads), lds, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace fa
