@@ -338,7 +338,11 @@ def main():
     else:
         peak = PEAK_BF16_TFLOPS if w["dtype"] == "bf16" else PEAK_F32_TFLOPS
         value, unit, achieved = tflops, "TFLOP/s", tflops
-        metric = "attention fwd TFLOP/s and % of bf16 MFMA peak, 1 MI355X, N=8192 d=128 causal"
+        if args.workload == "headline":
+            metric = "attention fwd TFLOP/s and % of bf16 MFMA peak, 1 MI355X, N=8192 d=128 causal"
+        else:
+            metric = "attention fwd TFLOP/s and %% of %s MFMA peak, 1 MI355X, N=%d d=%d %s" % (
+                w["dtype"], N, d, "causal" if w["causal"] else "non-causal")
         clk = getattr(props, "clock_rate", 0) or 0     # kHz, as the runtime reports it
         if clk:
             log("bf16 dense peak from the device: %d CUs x %.0f MHz x 4096 FLOP/clk = %.1f "

@@ -159,16 +159,18 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
 
 /*
  * fa_query_tile_rows -- query rows one workgroup of fa_fwd / fa_fwd_ex
- * processes for these arguments (block_n as in fa_opts, 0 = library choice):
- * the rows that share each key/value tile staged in on-chip memory, since
- * query rows are independent ("2.2b", "Scaling to Multiple Queries").  Under
- * causality a workgroup visits the key tiles up to the diagonal of the last
- * row of its query tile, so a trace has one entry per such tile.  Returns a
- * positive row count, or FA_ERR_SHAPE (N_q < 1) / FA_ERR_HEAD_DIM /
- * FA_ERR_DTYPE / FA_ERR_TILE.  Pure function of its arguments: no device
- * call.
+ * processes for these arguments (block_n as in fa_opts, 0 = library choice;
+ * causal nonzero or 0): the rows that share each key/value tile staged in
+ * on-chip memory, since query rows are independent ("2.2b", "Scaling to
+ * Multiple Queries").  128 or 256; the library takes 256 only for bfloat16,
+ * d = 128, 64-key tiles, N_q > 128 and enough workgroups to fill the GPU
+ * without one long causal workgroup deciding the run time.  Under causality
+ * a workgroup visits the key tiles up to the diagonal of the last row of its
+ * query tile, so a trace has one entry per such tile.  Returns the row
+ * count, or FA_ERR_SHAPE (B, H or N_q < 1) / FA_ERR_HEAD_DIM / FA_ERR_DTYPE /
+ * FA_ERR_TILE.  Pure function of its arguments: no device call.
  */
-int fa_query_tile_rows(int dtype, int d, int N_q, int block_n);
+int fa_query_tile_rows(int dtype, int B, int H, int N_q, int d, int block_n, int causal);
 
 /*
  * Split-key forward pass and the merge of partial states.

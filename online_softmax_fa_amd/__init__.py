@@ -93,7 +93,7 @@ def load_library(path=LIB_PATH):
     lib.fa_softmax_rows.restype = ci
     lib.fa_softmax_rows.argtypes = [vp, vp, vp, vp, i64, i64, ci, vp]
     lib.fa_query_tile_rows.restype = ci
-    lib.fa_query_tile_rows.argtypes = [ci, ci, ci, ci]
+    lib.fa_query_tile_rows.argtypes = [ci, ci, ci, ci, ci, ci, ci]
     _lib = lib
     return lib
 
@@ -134,9 +134,10 @@ def fa_fwd_ex(q, k, v, o, lse, B, H, N_q, N_k, d, scale, causal, kv_len_mask, dt
     _check(rc)
 
 
-def fa_query_tile_rows(dtype, d, N_q, block_n=0):
+def fa_query_tile_rows(dtype, B, H, N_q, d, block_n=0, causal=False):
     """C fa_query_tile_rows: query rows per workgroup of fa_fwd."""
-    rc = load_library().fa_query_tile_rows(int(dtype), int(d), int(N_q), int(block_n))
+    rc = load_library().fa_query_tile_rows(int(dtype), int(B), int(H), int(N_q), int(d),
+                                           int(block_n), int(bool(causal)))
     if rc < 0:
         _check(rc)
     return int(rc)

@@ -207,14 +207,14 @@ size_t fa_splitkv_workspace_bytes(int B, int H, int N_q, int d, int num_splits)
     return total;
 }
 
-int fa_query_tile_rows(int dtype, int d, int N_q, int block_n)
+int fa_query_tile_rows(int dtype, int B, int H, int N_q, int d, int block_n, int causal)
 {
-    if (N_q <= 0) return FA_ERR_SHAPE;
+    if (B <= 0 || H <= 0 || N_q <= 0) return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
     if (block_n != 0 && block_n != 16 && block_n != 32 && block_n != 64 && block_n != 128)
         return FA_ERR_TILE;
-    return fa::query_tile_rows(dtype, block_n == 0 ? 64 : block_n, N_q);
+    return fa::query_tile_rows(dtype, d, block_n == 0 ? 64 : block_n, B, H, N_q, causal ? 1 : 0, 1);
 }
 
 int fa_splitkv_splits(int B, int H, int N_q, int N_k, int d, int causal)
@@ -231,7 +231,7 @@ int fa_splitkv_splits(int B, int H, int N_q, int N_k, int d, int causal)
     // Four workgroups per compute unit keep every unit busy with work queued
     // behind the resident ones (query tiles of the bf16 kernel).
     const double target = 4.0 * cus;
-    const int64_t bm = fa::query_tile_rows(FA_DTYPE_BF16, kSplitBlockN, N_q);
+    const int64_t bm = fa::query_tile_rows(FA_DTYPE_BF16, d, kSplitBlockN, B, H, N_q, causal ? 1 : 0, 1);
     const double wgs = (double)B * H * (((int64_t)N_q + bm - 1) / bm);
     if (wgs >= target) return 1;
     const int64_t keys = causal ? (N_q < N_k ? N_q : N_k) : N_k;

@@ -39,8 +39,9 @@ struct Params {
 };
 
 // Query rows per workgroup of the forward kernel for validated arguments
-// (dtype 0 = fp32, 1 = bf16; block_n 16, 32, 64 or 128; n_q >= 1).
-int query_tile_rows(int dtype, int block_n, int n_q);
+// (dtype 0 = fp32, 1 = bf16; d 64 or 128; block_n 16, 32, 64 or 128; B, H,
+// n_q >= 1; n_split key ranges per query tile, 1 for the plain pass).
+int query_tile_rows(int dtype, int d, int block_n, int B, int H, int n_q, int causal, int n_split);
 
 // Enqueues the forward kernel for validated arguments.  dtype: 0 = fp32,
 // 1 = bf16; d: 64 or 128; block_n: 16, 32, 64 or 128.

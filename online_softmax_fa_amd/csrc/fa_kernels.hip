@@ -112,13 +112,22 @@ __device__ __forceinline__ bool lazy_step(f32x16 (&s)[NKB], bf16x8 (&pb)[NT16], 
 // ---------------------------------------------------------------------------
 // bf16 kernel
 // ---------------------------------------------------------------------------
-// Waves per workgroup of the bf16 kernel: 8 (two per SIMD, one workgroup per
-// CU), so that each K/V tile staged in LDS serves 256 query rows; 4 for
-// 128-key tiles, whose score registers do not fit the 256 VGPRs a wave
-// may use when two share a SIMD, and for at most 128 query rows, which
-// cannot occupy 8 waves: there two 4-wave workgroups per CU keep twice the
-// K/V transfers in flight (decoding is bound by reading K and V).
-constexpr int bf16_waves(int bn, int nq) { return bn == 128 || nq <= 128 ? 4 : 8; }
+// Waves per workgroup of the bf16 kernel: 4 (query tiles of 128 rows, one
+// wave per SIMD and workgroup, two or more workgroups per CU), or 8 (256
+// rows, two waves per SIMD, one workgroup per CU), which serves every K/V
+// tile staged in LDS to twice the rows.  8 waves pay off only for d = 128
+// with 64-key tiles and when there are enough workgroups that none of them
+// is the critical path: causal workgroups differ in length (the last query
+// tile visits every key tile), so there it takes 8 per CU; equal-length
+// non-causal ones need only fill the CUs.  gfx950 parts have 256 CUs.
+constexpr int kComputeUnits = 256;
+
+inline int bf16_waves(int d, int bn, int64_t B, int64_t H, int64_t nq, bool causal, int n_split)
+{
+    if (d != 128 || bn != 64 || nq <= 128) return 4;
+    const int64_t wgs = B * H * ((nq + 255) / 256) * n_split;
+    return wgs >= (causal ? 8 : 1) * (int64_t)kComputeUnits ? 8 : 4;
+}
 
 template <int D, int BN, int NW>
 struct Bf16Cfg {
@@ -922,12 +931,11 @@ static hipError_t dispatch_bf16_nw(const Params &p0, int causal, int B, int H, h
 template <int D, int BN>
 static hipError_t dispatch_bf16(const Params &p, int causal, int B, int H, hipStream_t stream)
 {
-    if constexpr (BN == 128)
-        return dispatch_bf16_nw<D, BN, 4>(p, causal, B, H, stream);
-    else if (bf16_waves(BN, p.Nq) == 4)
-        return dispatch_bf16_nw<D, BN, 4>(p, causal, B, H, stream);
-    else
-        return dispatch_bf16_nw<D, BN, 8>(p, causal, B, H, stream);
+    if constexpr (D == 128 && BN == 64) {
+        if (bf16_waves(D, BN, B, H, p.Nq, causal != 0, p.n_split) == 8)
+            return dispatch_bf16_nw<D, BN, 8>(p, causal, B, H, stream);
+    }
+    return dispatch_bf16_nw<D, BN, 4>(p, causal, B, H, stream);
 }
 
 template <int D, int BN>
@@ -961,9 +969,9 @@ static hipError_t dispatch_d(const Params &p, int dtype, int block_n, int causal
     }
 }
 
-int query_tile_rows(int dtype, int block_n, int n_q)
+int query_tile_rows(int dtype, int d, int block_n, int B, int H, int n_q, int causal, int n_split)
 {
-    return dtype == 1 ? 32 * bf16_waves(block_n, n_q) : 32 * 4;
+    return dtype == 1 ? 32 * bf16_waves(d, block_n, B, H, n_q, causal != 0, n_split) : 32 * 4;
 }
 
 hipError_t launch_fwd(const Params &p, int dtype, int d, int block_n, int causal, int B, int H,

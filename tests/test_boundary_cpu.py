@@ -35,20 +35,31 @@ def test_header_declares_the_entry_points():
 
 
 def test_query_tile_rows(lib):
-    """Rows per workgroup: a whole number of 32-row wave tiles, fixed by the
-    arguments alone (no device needed); bad arguments give their status."""
-    for dtype in (fa.FA_DTYPE_F32, fa.FA_DTYPE_BF16):
+    """Rows per workgroup: 128 or 256, fixed by the arguments alone (no device
+    needed); 256 only for bf16 with d = 128, 64-key tiles and enough
+    workgroups (the headline and long-context shapes); bad arguments give
+    their status."""
+    F32, BF16 = fa.FA_DTYPE_F32, fa.FA_DTYPE_BF16
+    q = lib.fa_query_tile_rows
+    for dtype in (F32, BF16):
         for d in (64, 128):
             for nq in (1, 128, 129, 8192):
                 for bn in (0, 16, 32, 64, 128):
-                    r = lib.fa_query_tile_rows(dtype, d, nq, bn)
-                    assert r > 0 and r % 32 == 0
-                assert (lib.fa_query_tile_rows(dtype, d, nq, 0) ==
-                        lib.fa_query_tile_rows(dtype, d, nq, 64))
-    assert lib.fa_query_tile_rows(fa.FA_DTYPE_BF16, 64, 0, 64) == fa.FA_ERR_SHAPE
-    assert lib.fa_query_tile_rows(fa.FA_DTYPE_BF16, 96, 8, 64) == fa.FA_ERR_HEAD_DIM
-    assert lib.fa_query_tile_rows(7, 64, 8, 64) == fa.FA_ERR_DTYPE
-    assert lib.fa_query_tile_rows(fa.FA_DTYPE_BF16, 64, 8, 48) == fa.FA_ERR_TILE
+                    for causal in (0, 1):
+                        assert q(dtype, 2, 32, nq, d, bn, causal) in (128, 256)
+                assert q(dtype, 2, 32, nq, d, 0, 1) == q(dtype, 2, 32, nq, d, 64, 1)
+    assert q(BF16, 2, 32, 8192, 128, 64, 1) == 256          # headline, causal
+    assert q(BF16, 1, 8, 32768, 128, 64, 0) == 256          # long context, non-causal
+    assert q(BF16, 2, 32, 4096, 128, 64, 1) == 128          # causal, too few workgroups
+    assert q(BF16, 2, 32, 8192, 64, 64, 1) == 128           # d = 64
+    assert q(BF16, 2, 32, 8192, 128, 32, 1) == 128          # other tile sizes
+    assert q(BF16, 256, 8, 128, 128, 64, 0) == 128          # N_q <= 128
+    assert q(F32, 2, 32, 8192, 128, 64, 1) == 128           # fp32 kernel
+    assert q(BF16, 1, 1, 0, 64, 64, 0) == fa.FA_ERR_SHAPE
+    assert q(BF16, 0, 1, 8, 64, 64, 0) == fa.FA_ERR_SHAPE
+    assert q(BF16, 1, 1, 8, 96, 64, 0) == fa.FA_ERR_HEAD_DIM
+    assert q(7, 1, 1, 8, 64, 64, 0) == fa.FA_ERR_DTYPE
+    assert q(BF16, 1, 1, 8, 64, 48, 0) == fa.FA_ERR_TILE
 
 
 def test_header_compiles_as_c_and_cxx(tmp_path):

@@ -195,12 +195,54 @@ def test_edge_shapes(dtype, shape):
         mask[0, : min(5, Nk)] = 0
     scale = inputs.default_scale(d)
     o_ref, lse_ref = run_oracle(q, k, v, scale, causal=causal, mask=mask)
-    # every tile size, each reached with both workgroup shapes (query tiles
-    # of 128 rows for N_q <= 128, 256 rows above; see fa_query_tile_rows)
     for bn in (16, 32, 64, 128):
         say("edge %s %s bn=%d" % (dtype, shape, bn))
         o, lse = run_gpu(q, k, v, scale, causal=causal, mask=mask, block_n=bn)
         compare(o, lse, o_ref, lse_ref, dtype, what="bn%d" % bn)
+
+
+# ---------------------------------------------------------------------------
+# 256-row workgroups (8 waves): bf16, d = 128, 64-key tiles and enough
+# workgroups -- ragged query and key tails, key-padding masks with fully
+# masked rows, the causal diagonal, both traversal orders
+# ---------------------------------------------------------------------------
+WIDE = [
+    # (B, H, Nq, Nk, causal, masked): 2*64*2 = 256 and 4*256*2 = 2048 workgroups
+    (2, 64, 300, 300, False, True),
+    (4, 256, 257, 257, True, False),
+]
+
+
+@pytest.mark.parametrize("shape", WIDE, ids=["%dx%dx%dx%d%s%s" % (s[:4] + ("c" if s[4] else "",
+                                                                         "m" if s[5] else ""))
+                                             for s in WIDE])
+def test_256_row_workgroups(shape):
+    import online_softmax_fa_amd as fa
+    B, H, Nq, Nk, causal, masked = shape
+    d = 128
+    assert fa.fa_query_tile_rows(fa.FA_DTYPE_BF16, B, H, Nq, d, 64, causal) == 256
+    seed = 5600 + H
+    q, k, v = inputs.gaussian_qkv(B, H, Nq, Nk, d, seed, 1.0, "bf16")
+    mask = None
+    if masked:
+        mask = inputs.bernoulli_mask(B, Nk, 0.3, seed + 1)
+        mask[1, :] = 0                      # batch 1: every row fully masked
+    scale = inputs.default_scale(d)
+    heads = [(0, 0), (0, H - 1), (B - 1, H // 2), (B - 1, H - 1)]
+    rows = sample_rows(B, H, Nq, heads, 96, seed + 2)
+    rows = np.unique(np.concatenate([rows, np.arange(Nq) + (H - 1) * Nq]))   # head (0, H-1) in full
+    o_ref, lse_ref = run_oracle(q, k, v, scale, causal=causal, mask=mask, rows=rows)
+    outs = []
+    for rev in (False, True):
+        say("256-row workgroups %s reverse=%d" % (shape, rev))
+        o, lse = run_gpu(q, k, v, scale, causal=causal, mask=mask, reverse_kv=rev)
+        compare(o.reshape(-1, d)[rows], lse.reshape(-1)[rows], o_ref, lse_ref, "bf16",
+                what="wide rev%d" % rev)
+        assert np.all(np.isfinite(o))
+        outs.append((o, lse))
+    if masked:
+        o, lse = outs[0]
+        assert np.all(o.reshape(B, H, Nq, d)[1] == 0.0) and np.all(np.isneginf(lse[1]))
 
 
 def test_fully_masked_batch_and_rows():

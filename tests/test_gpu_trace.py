@@ -81,7 +81,8 @@ def test_trace_of_adversarial_rows(dtype, bn, rev):
                 say("trace %s bn=%d rev=%d %s head %d row %d" % (dtype, bn, rev, name, h, row))
                 tr, _, _ = _trace(qd, kd, vd, scale, causal, md, bn, rev, 0, h, row)
                 bm = fa.fa_query_tile_rows(fa.FA_DTYPE_BF16 if dtype == "bf16" else fa.FA_DTYPE_F32,
-                                           q.shape[3], q.shape[2], bn)
+                                           q.shape[0], q.shape[1], q.shape[2], q.shape[3], bn,
+                                           causal)
                 n_t = _tiles_visited(row, N, bn, causal, bm)
                 assert np.all(np.isfinite(tr[:n_t, 0])) and np.all(np.isnan(tr[n_t:]))
                 s_row = scale * (kn[h] @ qn[h, row])
@@ -117,7 +118,8 @@ def test_trace_of_gaussian_causal_rows():
     qd, kd, vd = (x.to(DEV) for x in (q, k, v))
     for h, row in ((0, 0), (0, 129), (1, 1000), (1, 2047)):
         tr, _, _ = _trace(qd, kd, vd, scale, True, None, 64, False, 0, h, row)
-        n_t = _tiles_visited(row, N, 64, True, fa.fa_query_tile_rows(fa.FA_DTYPE_BF16, d, N, 64))
+        n_t = _tiles_visited(row, N, 64, True,
+                             fa.fa_query_tile_rows(fa.FA_DTYPE_BF16, B, H, N, d, 64, True))
         s_row = scale * (kn[h] @ qn[h, row])
         vis = np.arange(N) <= row
         ref = _oracle_trace(s_row, vis, 64, n_t, False)["trace"]
