@@ -70,6 +70,20 @@ def attention_flops(B, H, Nq, Nk, d, causal):
     return f / 2 if causal else f
 
 
+def visible_pairs(Nq, lengths, causal):
+    """(query, key) pairs of one head summed over sequences, with keys
+    j < L visible and, under causality, j <= i."""
+    total = 0
+    for L in lengths:
+        if not causal:
+            total += Nq * L
+        elif L >= Nq:
+            total += Nq * (Nq + 1) // 2
+        else:
+            total += L * (L + 1) // 2 + (Nq - L) * L
+    return total
+
+
 def algorithmic_bytes(B, H, Nq, Nk, d, esz):
     """Q, K, V read once; O and lse written once."""
     return B * H * (2 * Nq * d * esz + 2 * Nk * d * esz + Nq * 4)
@@ -96,6 +110,7 @@ def cpu_baseline(w, seconds):
 
     oracle.build(force=False)
     q, k, v = (x.float().numpy() for x in (w["q"], w["k"], w["v"]))
+    mask = None if w.get("mask") is None else w["mask"].numpy()
     B, H, N, d = w["B"], w["H"], w["N"], w["d"]
     Nq = w["Nq"]
     threads = len(os.sched_getaffinity(0))
@@ -113,8 +128,8 @@ def cpu_baseline(w, seconds):
     def timed(nrows):
         rows = np.linspace(0, total_rows - 1, nrows).astype(np.int64)
         t0 = time.perf_counter()
-        _, _, used = oracle.attn_fwd(q, k, v, w["scale"], causal=w["causal"], rows=rows,
-                                     threads=threads)
+        _, _, used = oracle.attn_fwd(q, k, v, w["scale"], causal=w["causal"], mask=mask,
+                                     rows=rows, threads=threads)
         return time.perf_counter() - t0, row_flops(rows), used
 
     n = max(threads, 16)
@@ -152,17 +167,21 @@ def cpu_tiled(w, seconds):
         x = t.reshape(B * H, -1, d)[:nh].contiguous()
         return x.view(torch.int16).numpy().view(np.uint16) if bf16 else x.numpy()
 
+    # with key-padding masks, heads of the first sequence only (one mask row)
+    mask = None if w.get("mask") is None else w["mask"][:1].numpy()
+    max_heads = B * H if mask is None else H
+
     def timed(nh):
         q, k, v = (arr(w[x], nh).reshape(1, nh, -1, d) for x in ("q", "k", "v"))
         t0 = time.perf_counter()
-        _, _, used = cpu.attention_cpu(q, k, v, w["scale"], w["causal"], None, threads,
+        _, _, used = cpu.attention_cpu(q, k, v, w["scale"], w["causal"], mask, threads,
                                        dtype="bf16" if bf16 else "f32")
         return time.perf_counter() - t0, used
 
     nh = 1
     dt, used = timed(nh)
-    if dt < seconds and nh < B * H:
-        nh = int(min(B * H, max(1, seconds / max(dt, 1e-3))))
+    if dt < seconds and nh < max_heads:
+        nh = int(min(max_heads, max(1, seconds / max(dt, 1e-3))))
         dt, used = timed(nh)
     esz = 2 if bf16 else 4
     if w.get("bound") == "hbm":
@@ -253,6 +272,9 @@ def main():
     ap.add_argument("--block-n", type=int, default=0)
     ap.add_argument("--splits", type=int, default=0,
                     help="decode: split count (0: the library's choice)")
+    ap.add_argument("--kv-lengths", action="store_true",
+                    help="key-padding prefix masks: per-sequence key lengths drawn uniformly "
+                         "from [N_k/2, N_k] (seed: the workload's + 1000)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
@@ -288,6 +310,12 @@ def main():
     log("workload %s: B=%d H=%d N_q=%d N_k=%d d=%d %s causal=%d" % (
         args.workload, B, H, Nq, N, d, w["dtype"], w["causal"]))
     q, k, v = (x.to(dev) for x in (w["q"], w["k"], w["v"]))
+    mask_d, lens = None, None
+    if args.kv_lengths:
+        lens = inputs.kv_lengths(B, N, inputs.WORKLOADS[args.workload]["seed"] + 1000)
+        w["mask"] = inputs.prefix_mask(lens, N)
+        mask_d = w["mask"].to(dev)
+        log("key lengths per sequence: %s" % lens.tolist())
     o = torch.empty_like(q)
     lse = torch.empty(B, H, Nq, dtype=torch.float32, device=dev)
 
@@ -299,11 +327,11 @@ def main():
 
         def step():
             fa.attention_splitkv(q, k, v, scale=w["scale"], causal=w["causal"], num_splits=ns,
-                                 out=(o, lse), workspace=ws)
+                                 kv_len_mask=mask_d, out=(o, lse), workspace=ws)
     else:
         def step():
             fa.attention(q, k, v, scale=w["scale"], causal=w["causal"], block_n=args.block_n,
-                         out=(o, lse))
+                         kv_len_mask=mask_d, out=(o, lse))
 
     for _ in range(args.warmup):
         step()
@@ -387,6 +415,13 @@ def main():
     }
     if split:
         result["config"]["splits"] = ns
+    if lens is not None:
+        # the metric counts every (query, key) pair; the visible ones are fewer
+        vis = visible_pairs(Nq, lens.tolist(), w["causal"]) * H
+        result["config"]["kv_lengths"] = lens.tolist()
+        result["effective_tflops"] = round(4.0 * d * vis / (ms * 1e-3) / 1e12, 3)
+        log("effective: %.1f TFLOP/s over the visible (query, key) pairs" %
+            result["effective_tflops"])
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of rows ...")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -98,6 +98,9 @@ typedef enum fa_dtype {
  *                tile maximum, so they contribute exactly zero ("The math of
  *                FlashAttention", "Pitfalls in implementing the recurrence";
  *                tiled-attention interview answer, second paragraph).
+ *                Key tiles before the first or after the last visible key of
+ *                a batch are skipped outright (no transfer, no work): exact,
+ *                since their weights are all zero.
  *   dtype        an fa_dtype.  Accumulation is float32 for both; bf16 inputs
  *                feed bf16 matrix-core products, fp32 inputs fp32 ones.
  *   stream       a hipStream_t (NULL: the default stream).
@@ -136,9 +139,12 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  *               bfloat16, m lags it: the kernel moves its reference only when
  *               a tile's scores exceed it by more than 16 / (scale * log2 e),
  *               so running max - that bound <= m <= running max.  Tiles the
- *               kernel never visits (above the causal diagonal of the row's
- *               query tile, fa_query_tile_rows rows) leave their entries
- *               untouched.
+ *               kernel never visits leave their entries untouched: those
+ *               above the causal diagonal of the row's query tile
+ *               (fa_query_tile_rows rows) and, with kv_len_mask, those
+ *               before the tile of the first or after the tile of the last
+ *               visible key of the batch within the remaining range (all of
+ *               them when it has none).
  *   trace_b, trace_h, trace_row
  *               the traced row: batch, head and query index, each in range
  *               (else FA_ERR_ARG).  Ignored when trace is NULL.

@@ -174,6 +174,74 @@ __device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t 
 // included, has completed (expcnt and lgkmcnt fields left at their maximum).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Key-padding masks: the first and the last visible key (nonzero byte) of
+// row[k_lo .. k_hi), found by all T threads of the workgroup together.
+// Returns false when every key of the range is masked.  Every thread of the
+// workgroup must call it (it synchronises once); it reads only bytes inside
+// the range: aligned 4-byte words for the interior, single bytes for up to
+// three keys at either end.  The results are workgroup-uniform.
+template <int T>
+__device__ __forceinline__ bool visible_span(const uint8_t *row, int k_lo, int k_hi, int &first,
+                                             int &last)
+{
+    __shared__ int red[2 * (T / 64)];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int f = 0x7fffffff, l = -1;
+    const uintptr_t base = (uintptr_t)row;
+    const uintptr_t p0 = base + k_lo, p1 = base + k_hi;
+    const uintptr_t w0 = (p0 + 3) & ~(uintptr_t)3, w1 = p1 & ~(uintptr_t)3;
+    const uintptr_t head_end = w0 < p1 ? w0 : p1;
+    const uintptr_t tail_beg = w1 > head_end ? w1 : head_end;
+    // edge bytes: threads 0..2 the head, 3..5 the tail
+    if (tid < 3 && p0 + tid < head_end && row[k_lo + tid]) {
+        f = k_lo + tid;
+        l = f;
+    }
+    if (tid >= 3 && tid < 6 && tail_beg + (tid - 3) < p1) {
+        const int k = (int)(tail_beg - base) + (tid - 3);
+        if (row[k]) {
+            f = f < k ? f : k;
+            l = l > k ? l : k;
+        }
+    }
+    // interior words
+    const int nwd = w1 > w0 ? (int)((w1 - w0) >> 2) : 0;
+    const uint32_t *wp = reinterpret_cast<const uint32_t *>(w0);
+    const int k_w0 = (int)(w0 - base);
+    for (int i = tid; i < nwd; i += T) {
+        const uint32_t x = wp[i];
+        const uint32_t nz = ((x & 0x000000ffu) ? 1u : 0u) | ((x & 0x0000ff00u) ? 2u : 0u) |
+                            ((x & 0x00ff0000u) ? 4u : 0u) | ((x & 0xff000000u) ? 8u : 0u);
+        if (nz) {
+            const int k = k_w0 + 4 * i;
+            const int kf = k + __builtin_ctz(nz), kl = k + 31 - __builtin_clz(nz);
+            f = f < kf ? f : kf;
+            l = l > kl ? l : kl;
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const int fo = __shfl_xor(f, off), lo = __shfl_xor(l, off);
+        f = f < fo ? f : fo;
+        l = l > lo ? l : lo;
+    }
+    if (lane == 0) {
+        red[wv] = f;
+        red[T / 64 + wv] = l;
+    }
+    __syncthreads();
+    f = red[0];
+    l = red[T / 64];
+#pragma unroll
+    for (int i = 1; i < T / 64; ++i) {
+        f = f < red[i] ? f : red[i];
+        l = l > red[T / 64 + i] ? l : red[T / 64 + i];
+    }
+    first = __builtin_amdgcn_readfirstlane(f);
+    last = __builtin_amdgcn_readfirstlane(l);
+    return last >= 0;
+}
+
 template <int N>
 struct IntC {
     static constexpr int value = N;

@@ -109,6 +109,27 @@ __device__ __forceinline__ bool lazy_step(f32x16 (&s)[NKB], bf16x8 (&pb)[NT16], 
     return rescale;
 }
 
+// A key-padding mask can leave whole key tiles at either end of a
+// workgroup's range with no visible key.  The range shrinks to the tiles from
+// the first to the last visible key, or to none when every key is masked: a
+// tile without a visible key adds nothing to l or o~ (all its weights are 0),
+// so leaving it out is exact, and saves its transfers and its wait.  Every
+// thread of the workgroup calls this with the same arguments.
+template <int BN, int T>
+__device__ __forceinline__ void trim_to_visible(const uint8_t *Mg, int Nk, int &t_lo, int &n_t)
+{
+    if (!Mg || n_t <= 0) return;
+    const int64_t end = (int64_t)(t_lo + n_t) * BN;
+    const int k_hi = end < Nk ? (int)end : Nk;
+    int first, last;
+    if (visible_span<T>(Mg, t_lo * BN, k_hi, first, last)) {
+        t_lo = first / BN;
+        n_t = last / BN + 1 - t_lo;
+    } else {
+        n_t = 0;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // bf16 kernel
 // ---------------------------------------------------------------------------
@@ -238,6 +259,7 @@ struct Bf16Fwd {
         }
         t_lo = (int)((int64_t)split * n_all / p.n_split);
         n_t = (int)((int64_t)(split + 1) * n_all / p.n_split) - t_lo;
+        trim_to_visible<BN, C::T>(Mg, Nk, t_lo, n_t);
 
         // Per-lane LDS byte addresses (stage 0) of the MFMA operands.
         //   K (A operand of S^T = K.Q^T, 16 bytes): key row 32*kb + l31,
@@ -764,8 +786,9 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_f32_kernel(const Params p)
         const int need = last_q / BN + 1;
         n_all = need < n_all ? need : n_all;
     }
-    const int t_lo = (int)((int64_t)split * n_all / p.n_split);
-    const int n_t = (int)((int64_t)(split + 1) * n_all / p.n_split) - t_lo;
+    int t_lo = (int)((int64_t)split * n_all / p.n_split);
+    int n_t = (int)((int64_t)(split + 1) * n_all / p.n_split) - t_lo;
+    trim_to_visible<BN, C::T>(Mg, Nk, t_lo, n_t);
     const bool trace_on = TRACE && bh == p.trace_bh && p.trace_row >= qw0 && p.trace_row < qw0 + 32;
 
     float *Kl = ldsf;

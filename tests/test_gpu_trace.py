@@ -35,14 +35,21 @@ def _gpu():
     fa.load_library()
 
 
-def _tiles_visited(row, N, bn, causal, bm):
-    """Key tiles the row's workgroup visits: all of them, or under causality
-    those up to the diagonal of the last row of its query tile of bm rows."""
+def _tiles_visited(row, N, bn, causal, bm, mask_row=None):
+    """Key tiles the row's workgroup visits, as (first, count): all of them,
+    or under causality those up to the diagonal of the last row of its query
+    tile of bm rows; with a key-padding mask only those from the first to the
+    last visible key of that range (none if it has no visible key)."""
     n = (N + bn - 1) // bn
     if causal:
         q0 = row // bm * bm
         n = min(n, (min(q0 + bm, N) - 1) // bn + 1)
-    return n
+    if mask_row is None:
+        return 0, n
+    vis = np.flatnonzero(np.asarray(mask_row)[: min(N, n * bn)])
+    if len(vis) == 0:
+        return 0, 0
+    return vis[0] // bn, vis[-1] // bn + 1 - vis[0] // bn
 
 
 def _trace(qd, kd, vd, scale, causal, mask, bn, rev, b, h, row):
@@ -54,12 +61,17 @@ def _trace(qd, kd, vd, scale, causal, mask, bn, rev, b, h, row):
     return buf.cpu().numpy().reshape(-1, 4), o, lse
 
 
-def _oracle_trace(s_row, vis, bn, n_vis_tiles, rev):
-    keys = min(len(s_row), n_vis_tiles * bn)
-    order = list(range(n_vis_tiles))
+def _oracle_trace(s_row, vis, bn, t0, n_t, rev):
+    """The oracle's recurrence over key tiles t0 .. t0 + n_t - 1 (the keys
+    before and after them are masked), block indices renumbered to tiles."""
+    lo, hi = t0 * bn, min(len(s_row), (t0 + n_t) * bn)
+    order = list(range(n_t))
     if rev:
         order = order[::-1]
-    return online_attention_row(s_row[:keys], None, block=bn, order=order, visible=vis[:keys])
+    ref = online_attention_row(s_row[lo:hi], None, block=bn, order=order, visible=vis[lo:hi])
+    for e in ref["trace"]:
+        e["block"] += t0
+    return ref
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -73,7 +85,8 @@ def test_trace_of_adversarial_rows(dtype, bn, rev):
     qd, kd, vd = (x.to(DEV) for x in (q, k, v))
     N = k.shape[2]
     cases = inputs.adversarial_cases()
-    for name in ("nomask", "causal", "bern30"):
+    for name in ("nomask", "causal", "bern30", "mask_max_keys", "causal_prefix_masked",
+                 "all_masked"):
         mask, causal = cases[name]
         md = None if mask is None else mask.to(DEV)
         for h in (0, 2, 3):
@@ -83,13 +96,14 @@ def test_trace_of_adversarial_rows(dtype, bn, rev):
                 bm = fa.fa_query_tile_rows(fa.FA_DTYPE_BF16 if dtype == "bf16" else fa.FA_DTYPE_F32,
                                            q.shape[0], q.shape[1], q.shape[2], q.shape[3], bn,
                                            causal)
-                n_t = _tiles_visited(row, N, bn, causal, bm)
+                t0, n_t = _tiles_visited(row, N, bn, causal, bm,
+                                         None if mask is None else mask[0].numpy())
                 assert np.all(np.isfinite(tr[:n_t, 0])) and np.all(np.isnan(tr[n_t:]))
                 s_row = scale * (kn[h] @ qn[h, row])
                 vis = np.ones(N, bool) if mask is None else mask[0].numpy().astype(bool)
                 if causal:
                     vis &= np.arange(N) <= row
-                ref = _oracle_trace(s_row, vis, bn, n_t, rev)["trace"]
+                ref = _oracle_trace(s_row, vis, bn, t0, n_t, rev)["trace"]
                 assert [int(t) for t in tr[:n_t, 0]] == [e["block"] for e in ref]
                 for e, (t, m, l, _) in zip(ref, tr[:n_t]):
                     if e["m_new"] == -math.inf:
@@ -118,11 +132,11 @@ def test_trace_of_gaussian_causal_rows():
     qd, kd, vd = (x.to(DEV) for x in (q, k, v))
     for h, row in ((0, 0), (0, 129), (1, 1000), (1, 2047)):
         tr, _, _ = _trace(qd, kd, vd, scale, True, None, 64, False, 0, h, row)
-        n_t = _tiles_visited(row, N, 64, True,
-                             fa.fa_query_tile_rows(fa.FA_DTYPE_BF16, B, H, N, d, 64, True))
+        t0, n_t = _tiles_visited(row, N, 64, True,
+                                 fa.fa_query_tile_rows(fa.FA_DTYPE_BF16, B, H, N, d, 64, True))
         s_row = scale * (kn[h] @ qn[h, row])
         vis = np.arange(N) <= row
-        ref = _oracle_trace(s_row, vis, 64, n_t, False)["trace"]
+        ref = _oracle_trace(s_row, vis, 64, t0, n_t, False)["trace"]
         for e, (t, m, l, _) in zip(ref, tr[:n_t]):
             if e["m_new"] == -math.inf:
                 assert m == -math.inf and l == 0.0
