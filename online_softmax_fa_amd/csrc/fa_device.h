@@ -23,15 +23,29 @@ static constexpr float kLn2 = 0.693147180559945309f;
 
 // ---------------------------------------------------------------------------
 // Grid mapping.  Workgroups are dispatched round-robin over the 8 XCDs
-// (workgroup g runs on XCD g % 8).  The logical index gives every XCD a
-// contiguous range of work items, ordered head by head, so the query tiles of
-// one (batch, head) run together on one XCD and share its L2 for K and V.
-// Within a head, causal query tiles go longest first.
+// (workgroup g runs on XCD g % 8), and each XCD takes its share in order of
+// g.  Work items are (batch-head, query tile, key range), key ranges
+// innermost.  Every XCD gets a contiguous range of them, so the query tiles of
+// one (batch, head) run on one XCD and share its L2 for K and V.  Under
+// causality query tile t visits t + 1 times the keys of tile 0, so item
+// lengths differ: each XCD then takes its items longest first across all of
+// its heads (query tiles from the last to the first, the heads within each),
+// and the free CUs that pick up the next item in that order finish together.
+// That needs the heads to divide evenly among the XCDs; otherwise the items
+// go head by head, each head's longest first.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int logical_tile(int g, int G)
+__device__ __forceinline__ int logical_tile(int g, int G, int n_qt, int n_split, bool causal)
 {
-    const int per = G >> 3, rem = G & 7;
     const int x = g & 7, j = g >> 3;
+    const int heads = G / (n_qt * n_split);
+    if (causal && (heads & 7) == 0) {
+        const int hp = heads >> 3;                 // heads per XCD
+        const int per_rank = hp * n_split;         // items per query-tile rank
+        const int r = j / per_rank, rest = j - r * per_rank;
+        const int hh = rest / n_split, sp = rest - hh * n_split;
+        return ((x * hp + hh) * n_qt + r) * n_split + sp;
+    }
+    const int per = G >> 3, rem = G & 7;
     return x * per + (x < rem ? x : rem) + j;
 }
 

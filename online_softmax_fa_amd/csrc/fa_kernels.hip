@@ -218,7 +218,7 @@ struct Bf16Fwd {
         h = lane >> 5;
 
         // work item L = (head, query tile, key range), key ranges innermost
-        const int L = logical_tile(blockIdx.x, gridDim.x);
+        const int L = logical_tile(blockIdx.x, gridDim.x, p.n_qt, p.n_split, CAUSAL);
         split = L % p.n_split;
         const int L2 = L / p.n_split;
         bh = L2 / p.n_qt;
@@ -753,7 +753,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_f32_kernel(const Params p)
     const int h = lane >> 5;
 
     // work item L = (head, query tile, key range), key ranges innermost
-    const int L = logical_tile(blockIdx.x, gridDim.x);
+    const int L = logical_tile(blockIdx.x, gridDim.x, p.n_qt, p.n_split, CAUSAL);
     const int split = L % p.n_split;
     const int L2 = L / p.n_split;
     const int bh = L2 / p.n_qt;
