@@ -139,15 +139,16 @@ __device__ __forceinline__ void trim_to_visible(const uint8_t *Mg, int Nk, int &
 // tile staged in LDS to twice the rows.  8 waves pay off only for d = 128
 // with 64-key tiles and when there are enough workgroups that none of them
 // is the critical path: causal workgroups differ in length (the last query
-// tile visits every key tile), so there it takes 8 per CU; equal-length
-// non-causal ones need only fill the CUs.  gfx950 parts have 256 CUs.
+// tile visits every key tile), so there it takes two per CU, which the
+// longest-first order packs evenly; equal-length non-causal ones need only
+// fill the CUs.  gfx950 parts have 256 CUs.
 constexpr int kComputeUnits = 256;
 
 inline int bf16_waves(int d, int bn, int64_t B, int64_t H, int64_t nq, bool causal, int n_split)
 {
     if (d != 128 || bn != 64 || nq <= 128) return 4;
     const int64_t wgs = B * H * ((nq + 255) / 256) * n_split;
-    return wgs >= (causal ? 8 : 1) * (int64_t)kComputeUnits ? 8 : 4;
+    return wgs >= (causal ? 2 : 1) * (int64_t)kComputeUnits ? 8 : 4;
 }
 
 template <int D, int BN, int NW>

@@ -50,7 +50,9 @@ def test_query_tile_rows(lib):
                 assert q(dtype, 2, 32, nq, d, 0, 1) == q(dtype, 2, 32, nq, d, 64, 1)
     assert q(BF16, 2, 32, 8192, 128, 64, 1) == 256          # headline, causal
     assert q(BF16, 1, 8, 32768, 128, 64, 0) == 256          # long context, non-causal
-    assert q(BF16, 2, 32, 4096, 128, 64, 1) == 128          # causal, too few workgroups
+    assert q(BF16, 2, 16, 4096, 128, 64, 1) == 256          # causal, 2 workgroups per CU
+    assert q(BF16, 1, 8, 8192, 128, 64, 1) == 128           # causal, too few workgroups
+    assert q(BF16, 1, 4, 8192, 128, 64, 0) == 128           # non-causal, too few workgroups
     assert q(BF16, 2, 32, 8192, 64, 64, 1) == 128           # d = 64
     assert q(BF16, 2, 32, 8192, 128, 32, 1) == 128          # other tile sizes
     assert q(BF16, 256, 8, 128, 128, 64, 0) == 128          # N_q <= 128
