@@ -26,23 +26,36 @@ static constexpr float kLn2 = 0.693147180559945309f;
 // (workgroup g runs on XCD g % 8), and each XCD takes its share in order of
 // g.  Work items are (batch-head, query tile, key range), key ranges
 // innermost.  Every XCD gets a contiguous range of them, so the query tiles of
-// one (batch, head) run on one XCD and share its L2 for K and V.  Under
-// causality query tile t visits t + 1 times the keys of tile 0, so item
-// lengths differ: each XCD then takes its items longest first across all of
-// its heads (query tiles from the last to the first, the heads within each),
-// and the free CUs that pick up the next item in that order finish together.
+// one (batch, head) run on one XCD and share its L2 for K and V.
+//
+// Under causality query tile t visits t + 1 times the keys of tile 0, so item
+// lengths differ, and a CU that finishes early takes the next item in
+// dispatch order.  Each XCD therefore goes through its heads in groups, and
+// within a group takes the items longest first across the group's heads
+// (query tiles from the last to the first, the heads within each): the CUs
+// then finish together.  A group is the fewest heads (a power of two) with at
+// least as many items as the XCD runs workgroups at once (`slots`), which
+// keeps the K/V the XCD reads at a time, and so its L2 footprint, small.
 // That needs the heads to divide evenly among the XCDs; otherwise the items
 // go head by head, each head's longest first.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int logical_tile(int g, int G, int n_qt, int n_split, bool causal)
+__device__ __forceinline__ int logical_tile(int g, int G, int n_qt, int n_split, bool causal,
+                                            int slots)
 {
     const int x = g & 7, j = g >> 3;
     const int heads = G / (n_qt * n_split);
     if (causal && (heads & 7) == 0) {
         const int hp = heads >> 3;                 // heads per XCD
-        const int per_rank = hp * n_split;         // items per query-tile rank
-        const int r = j / per_rank, rest = j - r * per_rank;
-        const int hh = rest / n_split, sp = rest - hh * n_split;
+        const int items = n_qt * n_split;          // items per head
+        int grp = 1;
+        while (grp < hp && grp * items < slots) grp *= 2;
+        grp = grp < hp ? grp : hp;
+        const int gi = j / (grp * items), jg = j - gi * grp * items;
+        const int h0 = gi * grp;
+        const int gs = hp - h0 < grp ? hp - h0 : grp;   // heads in this group
+        const int per_rank = gs * n_split;
+        const int r = jg / per_rank, rest = jg - r * per_rank;
+        const int hh = h0 + rest / n_split, sp = rest % n_split;
         return ((x * hp + hh) * n_qt + r) * n_split + sp;
     }
     const int per = G >> 3, rem = G & 7;

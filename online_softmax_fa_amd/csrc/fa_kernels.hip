@@ -176,6 +176,18 @@ struct Bf16Cfg {
     static constexpr int V_BASE = STAGES * TILE;
 };
 
+// Workgroups per CU the kernel is compiled for: two waves per SIMD (at most
+// 256 VGPRs per lane) when the LDS of that many workgroups fits, else one
+// workgroup.
+template <int D, int BN, int NW>
+constexpr int bf16_blocks_per_cu()
+{
+    const int by_waves = 8 / NW;
+    const int by_lds = 2 * Bf16Cfg<D, BN, NW>::LDS_BYTES <= 160 * 1024 ? 2 : 1;
+    const int b = by_waves < by_lds ? by_waves : by_lds;
+    return b < 1 ? 1 : b;
+}
+
 // Per-thread state and steps of the bf16 kernel.  The kernel body is a
 // struct with device member functions (no lambdas), all inlined.  TRACE
 // builds the variant that records one row's state after every tile
@@ -219,7 +231,8 @@ struct Bf16Fwd {
         h = lane >> 5;
 
         // work item L = (head, query tile, key range), key ranges innermost
-        const int L = logical_tile(blockIdx.x, gridDim.x, p.n_qt, p.n_split, CAUSAL);
+        const int L = logical_tile(blockIdx.x, gridDim.x, p.n_qt, p.n_split, CAUSAL,
+                                   kComputeUnits / 8 * bf16_blocks_per_cu<D, BN, NW>());
         split = L % p.n_split;
         const int L2 = L / p.n_split;
         bh = L2 / p.n_qt;
@@ -618,18 +631,6 @@ struct Bf16Fwd {
     }
 };
 
-// Workgroups per CU the kernel is compiled for: two waves per SIMD (at most
-// 256 VGPRs per lane) when the LDS of that many workgroups fits, else one
-// workgroup.
-template <int D, int BN, int NW>
-constexpr int bf16_blocks_per_cu()
-{
-    const int by_waves = 8 / NW;
-    const int by_lds = 2 * Bf16Cfg<D, BN, NW>::LDS_BYTES <= 160 * 1024 ? 2 : 1;
-    const int b = by_waves < by_lds ? by_waves : by_lds;
-    return b < 1 ? 1 : b;
-}
-
 template <int D, int BN, int NW, bool CAUSAL, bool TRACE>
 __global__ __launch_bounds__(NW * 64, (bf16_blocks_per_cu<D, BN, NW>())) void fa_fwd_bf16_kernel(
     const Params p)
@@ -754,7 +755,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_f32_kernel(const Params p)
     const int h = lane >> 5;
 
     // work item L = (head, query tile, key range), key ranges innermost
-    const int L = logical_tile(blockIdx.x, gridDim.x, p.n_qt, p.n_split, CAUSAL);
+    const int L = logical_tile(blockIdx.x, gridDim.x, p.n_qt, p.n_split, CAUSAL,
+                               kComputeUnits / 8 * 2);
     const int split = L % p.n_split;
     const int L2 = L / p.n_split;
     const int bh = L2 / p.n_qt;
