@@ -245,6 +245,50 @@ def test_256_row_workgroups(shape):
         assert np.all(o.reshape(B, H, Nq, d)[1] == 0.0) and np.all(np.isneginf(lse[1]))
 
 
+def _span_mask(N):
+    """Key-padding masks whose visible keys sit inside the key range, so that
+    whole key tiles before and after them are skipped: batch 0 sees keys
+    150..529 only, batch 1 the single key 333, batch 2 the last 3 keys.  With
+    N odd the mask rows start at unaligned byte offsets."""
+    m = torch.zeros(3, N, dtype=torch.uint8)
+    m[0, 150:530] = 1
+    m[1, 333] = 1
+    m[2, N - 3:] = 1
+    return m
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_mask_spans(dtype, d, causal):
+    """Visible keys only in the middle, at one key, or at the end of the key
+    range, at every tile size and both orders, and through the split-key
+    path: the tiles outside the span are never visited, and rows that see no
+    key get o = 0 and lse = -inf exactly."""
+    import online_softmax_fa_amd as fa
+    B, H, N = 3, 2, 701
+    q, k, v = inputs.gaussian_qkv(B, H, N, N, d, 5800 + d + causal, 1.0, dtype)
+    mask = _span_mask(N)
+    scale = inputs.default_scale(d)
+    o_ref, lse_ref = run_oracle(q, k, v, scale, causal=causal, mask=mask)
+    for bn in BLOCKS:
+        for rev in (False, True):
+            say("mask spans %s d=%d causal=%d bn=%d reverse=%d" % (dtype, d, causal, bn, rev))
+            o, lse = run_gpu(q, k, v, scale, causal=causal, mask=mask, block_n=bn, reverse_kv=rev)
+            compare(o, lse, o_ref, lse_ref, dtype, what="spans bn%d rev%d" % (bn, rev))
+            if causal:   # rows before the first visible key see nothing
+                assert np.all(o[0, :, :150] == 0) and np.all(np.isneginf(lse[0, :, :150]))
+                assert np.all(o[2, :, :N - 3] == 0) and np.all(np.isneginf(lse[2, :, :N - 3]))
+    dev = torch.device("cuda:0")
+    for ns in (2, 5):
+        say("mask spans split-key %s d=%d causal=%d splits=%d" % (dtype, d, causal, ns))
+        o, lse = fa.attention_splitkv(q.to(dev), k.to(dev), v.to(dev), scale=scale, causal=causal,
+                                      kv_len_mask=mask.to(dev), num_splits=ns)
+        torch.cuda.synchronize()
+        compare(o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy(), o_ref, lse_ref,
+                dtype, what="spans split %d" % ns)
+
+
 def test_fully_masked_batch_and_rows():
     B, H, N, d = 3, 2, 96, 64
     q, k, v = inputs.gaussian_qkv(B, H, N, N, d, 77, 1.0, "bf16")
