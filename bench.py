@@ -11,6 +11,8 @@ about 7% slower on the same device.
 Prints ONE JSON line on stdout (everything else goes to stderr):
   value      attention TFLOP/s = 4*B*H*N_q*N_k*d / t, halved for causal
   roofline   the kernel against the bf16 dense MFMA peak (2.5 PFLOP/s)
+  launch_ms  median and minimum of 20 steps timed one by one, after the
+             timed region (`value` and ms_per_step are the mean of the K)
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
              workload's rows, on this host's cores, in the same unit
 
@@ -68,6 +70,32 @@ def kernel_source_hash(workload):
 def attention_flops(B, H, Nq, Nk, d, causal):
     f = 4.0 * B * H * Nq * Nk * d
     return f / 2 if causal else f
+
+
+def per_launch_ms(step, stream, torch, n=20):
+    """Median and minimum of n steps timed one by one (an event pair around
+    each, on the stream the kernels run on), after the timed region."""
+    times = []
+    for _ in range(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+    return {"median": round(times[n // 2], 4), "min": round(times[0], 4), "launches": n}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def visible_pairs(Nq, lengths, causal):
@@ -146,6 +174,7 @@ def cpu_baseline(w, seconds):
         "unit": "GB/s" if hbm else "TFLOP/s",
         "cores": int(used),
         "kind": "oracle",
+        "cpu": cpu_model(),
         "sample": "%d of %d query rows (evenly spaced over all heads), fp64 three-pass "
                   "oracle, %.1f s wall" % (n, total_rows, dt),
     }
@@ -189,6 +218,7 @@ def cpu_tiled(w, seconds):
     else:
         value, unit = nh * attention_flops(1, 1, Nq, N, d, w["causal"]) / dt / 1e12, "TFLOP/s"
     return {"value": value, "unit": unit, "cores": int(used), "kind": "cpu_tiled",
+            "cpu": cpu_model(),
             "sample": "%d of %d heads, libfa_cpu.so (the same recurrence, cache-tiled and "
                       "vectorized on the host), %.1f s wall" % (nh, B * H, dt)}
 
@@ -213,6 +243,7 @@ def softmax_cpu_baseline(s, seconds):
             break
     dt = time.perf_counter() - t0
     return {"value": done * nb / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": "%d of %d rows (evenly spaced), fp64 three-pass oracle, %.1f s wall" % (
                 done, rows, dt)}
 
@@ -239,6 +270,7 @@ def bench_softmax(args, torch, fa, inputs):
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
+    launch_ms = per_launch_ms(step, stream, torch)
     nbytes = 2 * rows * n * s.element_size() + 2 * rows * 4
     gbs = nbytes / (ms * 1e-3) / 1e9
     log("%.3f ms/step, %.1f GB/s = %.1f%% of %.0f GB/s" % (ms, gbs, 100 * gbs / PEAK_HBM_GBS,
@@ -251,6 +283,7 @@ def bench_softmax(args, torch, fa, inputs):
         "config": {"workload": "%s: %d rows x %d %s scores ~ N(0,%g^2)" % (
             args.workload, rows, n, w["dtype"], w["std"]), "rows": rows, "n": n},
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "launch_ms": launch_ms,
         "algorithmic_bytes_per_step": nbytes,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
@@ -349,6 +382,7 @@ def main():
     t_wall = time.perf_counter() - t_wall0
     ms_total = ev0.elapsed_time(ev1)
     ms = ms_total / args.steps
+    launch_ms = per_launch_ms(step, stream, torch)
     log("timed %d steps: %.3f ms/step (events), %.3f ms/step (wall)" % (
         args.steps, ms, 1e3 * t_wall / args.steps))
 
@@ -401,6 +435,7 @@ def main():
             "block_n": args.block_n or 64,
         },
         "pct_of_peak": round(100 * value / peak, 2),
+        "launch_ms": launch_ms,
         "tflops": round(tflops, 3),
         "algorithmic_bytes_per_step": nbytes,
         "roofline": {
