@@ -174,16 +174,21 @@ struct Bf16Cfg {
     // (the V base included in them), which stays within the 16-bit offset
     // field of the LDS instructions.
     static constexpr int V_BASE = STAGES * TILE;
+    // d = 64 with tiles of at most 32 keys fits in 128 VGPRs with shallower
+    // operand prefetch, and runs four waves per SIMD: the softmax-heavy small
+    // head width gains more from the extra waves than from deeper prefetch.
+    static constexpr bool LEAN = D == 64 && BN <= 32;
 };
 
 // Workgroups per CU the kernel is compiled for: two waves per SIMD (at most
-// 256 VGPRs per lane) when the LDS of that many workgroups fits, else one
-// workgroup.
+// 256 VGPRs per lane), or four for the lean configuration (at most 128), as
+// far as the LDS of that many workgroups (tiles plus 1 KiB of static LDS)
+// fits in the CU's 160 KiB.
 template <int D, int BN, int NW>
 constexpr int bf16_blocks_per_cu()
 {
-    const int by_waves = 8 / NW;
-    const int by_lds = 2 * Bf16Cfg<D, BN, NW>::LDS_BYTES <= 160 * 1024 ? 2 : 1;
+    const int by_waves = (Bf16Cfg<D, BN, NW>::LEAN ? 16 : 8) / NW;
+    const int by_lds = (int)((160 * 1024) / (Bf16Cfg<D, BN, NW>::LDS_BYTES + 1024));
     const int b = by_waves < by_lds ? by_waves : by_lds;
     return b < 1 ? 1 : b;
 }
@@ -440,7 +445,7 @@ struct Bf16Fwd {
         // of their use: a bounded number of live fragments, and the LDS
         // latency is hidden behind the matrix cores.
         {
-            constexpr int NM = D / 16 * C::NKB, PF = NM / 2;
+            constexpr int NM = D / 16 * C::NKB, PF = C::LEAN ? NM / 4 : NM / 2;
             __builtin_amdgcn_sched_group_barrier(0x100, PF, 5);
 #pragma unroll
             for (int i = 0; i < NM - PF; ++i) {
@@ -506,7 +511,7 @@ struct Bf16Fwd {
         // softmax below hides their LDS latency; the product loop then keeps
         // VA products' operands in flight.
         constexpr int NPV = C::NT16 * (D / 32);
-        constexpr int VA_MAX = C::NKB >= 4 ? 2 : 4;        // fewer where the scores take more registers
+        constexpr int VA_MAX = (C::NKB >= 4 || C::LEAN) ? 2 : 4;   // fewer where registers are short
         constexpr int VA = NPV < VA_MAX ? NPV : VA_MAX;
         bf16x8 vf[NPV];
         __builtin_amdgcn_sched_barrier(0);
@@ -994,6 +999,8 @@ static hipError_t dispatch_d(const Params &p, int dtype, int block_n, int causal
     default: return dispatch_f32<D, 64>(p, causal, B, H, s);
     }
 }
+
+int default_block_n(int dtype, int d) { return dtype == 1 && d == 64 ? 32 : 64; }
 
 int query_tile_rows(int dtype, int d, int block_n, int B, int H, int n_q, int causal, int n_split)
 {
