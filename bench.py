@@ -432,7 +432,7 @@ def main():
                 args.workload, B, H, Nq, N, d, w["dtype"],
                 "causal" if w["causal"] else "non-causal", w["std"]),
             "B": B, "H": H, "N_q": Nq, "N_k": N, "d": d, "causal": bool(w["causal"]),
-            "block_n": args.block_n or "library choice",
+            "block_n": args.block_n or 64,
         },
         "pct_of_peak": round(100 * value / peak, 2),
         "launch_ms": launch_ms,

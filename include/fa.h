@@ -117,20 +117,19 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
 /*
  * Test hooks.  A zeroed struct (or a NULL pointer) gives fa_fwd's behaviour.
  *
- *   block_n     keys per tile of the recurrence: 0 (library choice: 32 for
- *               bfloat16 with d = 64, else 64), 16, 32, 64 or 128.  The
- *               result must not depend on it ("The math of FlashAttention",
- *               "Proof of exactness": block size never enters the result;
- *               the tiled-attention interview answer asks to vary the tile
- *               size when testing).
+ *   block_n     keys per tile of the recurrence: 0 (library choice, 64), 16,
+ *               32, 64 or 128.  The result must not depend on it ("The math
+ *               of FlashAttention", "Proof of exactness": block size never
+ *               enters the result; the tiled-attention interview answer asks
+ *               to vary the tile size when testing).
  *   reverse_kv  nonzero: visit the key tiles last to first.  The result must
  *               not depend on the order either ("The running state": blocks
  *               may be processed in any order).
  *   trace       NULL, or a device array of ceil(N_k / block_n) * 4 floats
- *               (block_n as used: the library's choice for 0) that receives
- *               the running state of ONE query row after every key tile the
- *               kernel visits -- the per-block (m, l) printout the
- *               tiled-attention interview answer recommends for debugging.  Entry i (the i-th tile
+ *               (block_n as used, 64 for 0) that receives the running state
+ *               of ONE query row after every key tile the kernel visits --
+ *               the per-block (m, l) printout the tiled-attention interview
+ *               answer recommends for debugging.  Entry i (the i-th tile
  *               visited) is {tile index, m, l, 0}: l is the row's running
  *               denominator stated against the reference m, given in raw
  *               score units (q . k, before `scale`), so that after the tile

@@ -302,8 +302,7 @@ def attention(q, k, v, scale=None, causal=False, kv_len_mask=None, block_n=0, re
         buf, tb, th, trow = trace
         if buf.dtype != torch.float32 or not buf.is_cuda or not buf.is_contiguous():
             raise FaError(FA_ERR_SHAPE, "the trace buffer must be a contiguous float32 GPU tensor")
-        # block_n = 0: the library's choice, as include/fa.h states it
-        bn = int(block_n) or (32 if dt == FA_DTYPE_BF16 and d == 64 else 64)
+        bn = int(block_n) or 64
         if buf.numel() < (Nk + bn - 1) // bn * 4:
             raise FaError(FA_ERR_SHAPE, "the trace buffer needs ceil(N_k / block_n) * 4 floats")
         opts.trace, opts.trace_b, opts.trace_h, opts.trace_row = buf.data_ptr(), tb, th, trow

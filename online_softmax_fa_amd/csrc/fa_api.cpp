@@ -152,7 +152,7 @@ int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, i
     int block_n = opts ? opts->block_n : 0;
     if (block_n != 0 && block_n != 16 && block_n != 32 && block_n != 64 && block_n != 128)
         return FA_ERR_TILE;
-    if (block_n == 0) block_n = fa::default_block_n(dtype, d);
+    if (block_n == 0) block_n = 64;
 
     float *trace = opts ? opts->trace : nullptr;
     if (trace) {
@@ -214,8 +214,7 @@ int fa_query_tile_rows(int dtype, int B, int H, int N_q, int d, int block_n, int
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
     if (block_n != 0 && block_n != 16 && block_n != 32 && block_n != 64 && block_n != 128)
         return FA_ERR_TILE;
-    return fa::query_tile_rows(dtype, d, block_n == 0 ? fa::default_block_n(dtype, d) : block_n, B,
-                               H, N_q, causal ? 1 : 0, 1);
+    return fa::query_tile_rows(dtype, d, block_n == 0 ? 64 : block_n, B, H, N_q, causal ? 1 : 0, 1);
 }
 
 int fa_splitkv_splits(int B, int H, int N_q, int N_k, int d, int causal)

@@ -38,10 +38,6 @@ struct Params {
     int trace_row;        // its query index
 };
 
-// Keys per tile of the forward kernel when the caller passes block_n = 0:
-// 32 for bf16 with d = 64 (the lean four-waves-per-SIMD kernel), else 64.
-int default_block_n(int dtype, int d);
-
 // Query rows per workgroup of the forward kernel for validated arguments
 // (dtype 0 = fp32, 1 = bf16; d 64 or 128; block_n 16, 32, 64 or 128; B, H,
 // n_q >= 1; n_split key ranges per query tile, 1 for the plain pass).

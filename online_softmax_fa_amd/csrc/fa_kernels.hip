@@ -174,20 +174,22 @@ struct Bf16Cfg {
     // (the V base included in them), which stays within the 16-bit offset
     // field of the LDS instructions.
     static constexpr int V_BASE = STAGES * TILE;
-    // d = 64 with tiles of at most 32 keys fits in 128 VGPRs with shallower
-    // operand prefetch, and runs four waves per SIMD: the softmax-heavy small
-    // head width gains more from the extra waves than from deeper prefetch.
-    static constexpr bool LEAN = D == 64 && BN <= 32;
+    // Waves per SIMD the kernel is compiled for: two (at most 256 VGPRs per
+    // lane), except for d = 64, which with shallower operand prefetch fits
+    // three (64-key tiles, at most 168 VGPRs) or four (shorter tiles, 128):
+    // the softmax-heavy small head width gains more from the extra waves
+    // than from deeper prefetch.
+    static constexpr int WAVES_PER_SIMD = D == 64 ? (BN <= 32 ? 4 : (BN == 64 ? 3 : 2)) : 2;
+    static constexpr bool LEAN = WAVES_PER_SIMD > 2;
 };
 
-// Workgroups per CU the kernel is compiled for: two waves per SIMD (at most
-// 256 VGPRs per lane), or four for the lean configuration (at most 128), as
-// far as the LDS of that many workgroups (tiles plus 1 KiB of static LDS)
-// fits in the CU's 160 KiB.
+// Workgroups per CU the kernel is compiled for: WAVES_PER_SIMD waves on each
+// of the 4 SIMDs, as far as the LDS of that many workgroups (tiles plus
+// 1 KiB of static LDS) fits in the CU's 160 KiB.
 template <int D, int BN, int NW>
 constexpr int bf16_blocks_per_cu()
 {
-    const int by_waves = (Bf16Cfg<D, BN, NW>::LEAN ? 16 : 8) / NW;
+    const int by_waves = Bf16Cfg<D, BN, NW>::WAVES_PER_SIMD * 4 / NW;
     const int by_lds = (int)((160 * 1024) / (Bf16Cfg<D, BN, NW>::LDS_BYTES + 1024));
     const int b = by_waves < by_lds ? by_waves : by_lds;
     return b < 1 ? 1 : b;
@@ -999,8 +1001,6 @@ static hipError_t dispatch_d(const Params &p, int dtype, int block_n, int causal
     default: return dispatch_f32<D, 64>(p, causal, B, H, s);
     }
 }
-
-int default_block_n(int dtype, int d) { return dtype == 1 && d == 64 ? 32 : 64; }
 
 int query_tile_rows(int dtype, int d, int block_n, int B, int H, int n_q, int causal, int n_split)
 {
