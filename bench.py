@@ -55,6 +55,7 @@ def log(*a):
 # counter summary is used only while these files are unchanged.
 TRAFFIC_SOURCES = {
     "softmax": ("fa_softmax.hip", "fa_internal.h"),
+    "decode": ("fa_decode.hip", "fa_kernels.hip", "fa_device.h", "fa_internal.h"),
 }
 DEFAULT_TRAFFIC_SOURCES = ("fa_kernels.hip", "fa_device.h", "fa_internal.h")
 

@@ -270,7 +270,13 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
     p.part_l = ws + (size_t)num_splits * sz.rows;
     p.part_o = reinterpret_cast<float *>(static_cast<char *>(workspace) + acc_off);
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    rc = launch_status(fa::launch_fwd(p, dtype, d, kSplitBlockN, causal ? 1 : 0, B, H, st));
+    // One query row per (batch, head) in bf16: the decoding pass, which streams
+    // K and V through registers (its offsets within a head are 32-bit);
+    // otherwise the forward kernel in split mode.
+    if (dtype == FA_DTYPE_BF16 && N_q == 1 && (int64_t)N_k * d * 2 < ((int64_t)1 << 31))
+        rc = launch_status(fa::launch_decode(p, d, causal ? 1 : 0, B, H, st));
+    else
+        rc = launch_status(fa::launch_fwd(p, dtype, d, kSplitBlockN, causal ? 1 : 0, B, H, st));
     if (rc != FA_OK) return rc;
     return launch_status(fa::launch_merge(p.part_m, p.part_l, p.part_o, num_splits, sz.rows, d,
                                           scale, o, lse, dtype, st));

@@ -269,6 +269,27 @@ __device__ __forceinline__ bool visible_span(const uint8_t *row, int k_lo, int k
     return last >= 0;
 }
 
+// A key-padding mask can leave whole key tiles at either end of a
+// workgroup's range with no visible key.  The range shrinks to the tiles from
+// the first to the last visible key, or to none when every key is masked: a
+// tile without a visible key adds nothing to l or o~ (all its weights are 0),
+// so leaving it out is exact, and saves its transfers and its wait.  Every
+// thread of the workgroup calls this with the same arguments.
+template <int BN, int T>
+__device__ __forceinline__ void trim_to_visible(const uint8_t *Mg, int Nk, int &t_lo, int &n_t)
+{
+    if (!Mg || n_t <= 0) return;
+    const int64_t end = (int64_t)(t_lo + n_t) * BN;
+    const int k_hi = end < Nk ? (int)end : Nk;
+    int first, last;
+    if (visible_span<T>(Mg, t_lo * BN, k_hi, first, last)) {
+        t_lo = first / BN;
+        n_t = last / BN + 1 - t_lo;
+    } else {
+        n_t = 0;
+    }
+}
+
 template <int N>
 struct IntC {
     static constexpr int value = N;

@@ -48,6 +48,11 @@ int query_tile_rows(int dtype, int d, int block_n, int B, int H, int n_q, int ca
 hipError_t launch_fwd(const Params &p, int dtype, int d, int block_n, int causal, int B, int H,
                       hipStream_t stream);
 
+// Enqueues the split-key partial pass for N_q = 1 and bf16 (decoding): the
+// workgroup of (b, h, split) writes the partial state of row b*H + h over its
+// key range, as the forward kernel does in split-key mode.
+hipError_t launch_decode(const Params &p, int d, int causal, int B, int H, hipStream_t stream);
+
 // Enqueues the merge of n_parts partial states per row (part-major layout of
 // fa_merge_states) into o (dtype 0 = fp32, 1 = bf16) and lse.
 hipError_t launch_merge(const float *m, const float *l, const float *acc, int n_parts,

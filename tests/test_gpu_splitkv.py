@@ -87,6 +87,20 @@ def test_splitkv_decode_shapes(d, Nq, Nk):
         compare(o, lse, o_ref, lse_ref, "bf16", what="splits %s" % splits)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_splitkv_single_row_causal(d):
+    """One query row under top-left causality sees key 0 alone, whatever the
+    key count and split."""
+    B, H, Nk = 2, 3, 1000
+    q, k, v = inputs.gaussian_qkv(B, H, 1, Nk, d, seed=2250 + d, dtype="bf16")
+    scale = inputs.default_scale(d)
+    o_ref, lse_ref = run_oracle(q, k, v, scale, causal=True)
+    for splits in (None, 1, 3):
+        say("single causal row d=%d splits=%s" % (d, splits))
+        o, lse = run_split(q, k, v, scale, causal=True, num_splits=splits)
+        compare(o, lse, o_ref, lse_ref, "bf16", what="causal row splits %s" % splits)
+
+
 @pytest.mark.parametrize("splits", [3, 5])
 def test_splitkv_causal_prefill(splits):
     """Causal rows over key ranges: query tiles near the top have fewer tiles
@@ -109,13 +123,15 @@ def test_splitkv_decode_workload_full_size():
     compare(o, lse, o_ref, lse_ref, "bf16", what="decode")
 
 
-def test_splitkv_workspace_holds_the_partial_states():
+@pytest.mark.parametrize("dtype,Nq,d", [("f32", 3, 64), ("bf16", 1, 64), ("bf16", 1, 128)])
+def test_splitkv_workspace_holds_the_partial_states(dtype, Nq, d):
     """The workspace layout documented in fa.h: m [S][rows], l [S][rows], acc
     [S][rows][d] at the next 256-byte boundary.  Each range's state must match
     the oracle's partial_state of that key range (compared through quantities
-    that do not depend on the reference: m*scale + ln l and acc / l)."""
-    B, H, Nq, Nk, d, S = 1, 2, 3, 1000, 64, 4
-    q, k, v = inputs.gaussian_qkv(B, H, Nq, Nk, d, seed=2400, dtype="f32")
+    that do not depend on the reference: m*scale + ln l and acc / l).  One
+    query row in bf16 runs the decoding pass."""
+    B, H, Nk, S = 1, 2, 1000, 4
+    q, k, v = inputs.gaussian_qkv(B, H, Nq, Nk, d, seed=2400, dtype=dtype)
     scale = inputs.default_scale(d)
     nbytes = fa.fa_splitkv_workspace_bytes(B, H, Nq, d, S)
     ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=DEV)   # NaN-filled
