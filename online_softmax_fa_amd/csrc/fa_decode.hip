@@ -55,7 +55,7 @@ template <int D>
 struct DecBuf {
     u32x4 k[DecCfg<D>::NI];
     u32x4 v[DecCfg<D>::NI];
-    uint32_t mk;             // key-padding byte of this lane's key (1 without a mask)
+    uint32_t mk;             // key-padding byte of this lane's key (ignored without a mask)
 };
 
 template <int D, bool CAUSAL>
@@ -66,7 +66,8 @@ struct Decode {
     int Nk;
     float c;
     const uint16_t *Kg, *Vg;
-    const uint8_t *Mg;       // the batch's key-padding row, or the K rows (bytes never 0 matter)
+    const uint8_t *Mg;       // the batch's key-padding row; without a mask any readable
+                             // address (the K rows), whose byte is ignored
     bool masked;
     float qf[8];             // dims 8e .. 8e+7 of the query row
     float m, l_part;         // running maximum (raw score units) and this lane's share of l
