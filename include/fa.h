@@ -66,7 +66,11 @@ typedef enum fa_status {
     FA_ERR_ALIAS = -9,     /* an output overlaps an input or another output      */
     FA_ERR_ARG = -10,      /* another argument is out of range: the traced row,
                               num_splits, n_parts                                */
-    FA_ERR_WORKSPACE = -11 /* workspace NULL or smaller than required            */
+    FA_ERR_WORKSPACE = -11,/* workspace NULL or smaller than required            */
+    FA_ERR_ALIGN = -12     /* a pointer is not aligned as its entry point needs:
+                              16 bytes for q, k, v, o, acc and the trace, 4 bytes
+                              for lse, m and l, the element size for the score
+                              rows s and p of fa_softmax_rows                    */
 } fa_status;
 
 typedef enum fa_dtype {

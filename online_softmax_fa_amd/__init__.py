@@ -42,6 +42,7 @@ FA_ERR_LAUNCH = -8
 FA_ERR_ALIAS = -9
 FA_ERR_ARG = -10
 FA_ERR_WORKSPACE = -11
+FA_ERR_ALIGN = -12
 
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1

@@ -57,6 +57,11 @@ struct Sizes {
 };
 
 // Checks shared by the forward entry points, in the documented order.
+bool misaligned(const void *ptr, uintptr_t bytes)
+{
+    return (reinterpret_cast<uintptr_t>(ptr) & (bytes - 1)) != 0;
+}
+
 int check_fwd_args(const void *q, const void *k, const void *v, void *o, float *lse, int B,
                    int H, int N_q, int N_k, int d, float scale, const uint8_t *kv_len_mask,
                    int dtype, int n_split, Sizes &sz)
@@ -66,6 +71,10 @@ int check_fwd_args(const void *q, const void *k, const void *v, void *o, float *
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
     if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_SCALE;
+    // The kernels move q, k, v and o in 16-byte vectors and lse in words.
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
+        misaligned(lse, 4))
+        return FA_ERR_ALIGN;
 
     // Index space: every element offset must fit in int64, and the grid
     // (B*H*ceil(N_q/32)*n_split workgroups at most) in int32.
@@ -161,6 +170,7 @@ int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, i
             return FA_ERR_ARG;
         const size_t tb = (size_t)((N_k + block_n - 1) / block_n) * 4 * sizeof(float);
         if (overlaps_fwd(trace, tb, q, k, v, o, lse, kv_len_mask, sz)) return FA_ERR_ALIAS;
+        if (misaligned(trace, 16)) return FA_ERR_ALIGN;   // one 16-byte entry per tile
     }
 
     rc = check_device();
@@ -290,6 +300,9 @@ int fa_merge_states(const float *m, const float *l, const float *acc, int n_part
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
     if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_SCALE;
+    if (misaligned(acc, 16) || misaligned(o, 16) || misaligned(m, 4) || misaligned(l, 4) ||
+        misaligned(lse, 4))
+        return FA_ERR_ALIGN;
     if (n_parts < 1) return FA_ERR_ARG;
     if ((double)n_parts * rows * d * sizeof(float) > 9.0e18) return FA_ERR_SHAPE;
     const size_t mlb = (size_t)n_parts * rows * sizeof(float);
@@ -314,6 +327,8 @@ int fa_softmax_rows(const void *s, void *p, float *m, float *l, int64_t rows, in
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
     const size_t esz = dtype == FA_DTYPE_BF16 ? 2 : 4;
     if ((double)rows * n * esz > 9.0e18) return FA_ERR_SHAPE;
+    if (misaligned(s, esz) || misaligned(p, esz) || misaligned(m, 4) || misaligned(l, 4))
+        return FA_ERR_ALIGN;
     const size_t sb = (size_t)rows * n * esz, vb = (size_t)rows * sizeof(float);
     if (p != s && overlaps(p, sb, s, sb)) return FA_ERR_ALIAS;
     const void *bufs[2] = {s, p};
@@ -345,6 +360,9 @@ const char *fa_strerror(int code)
         break;
     case FA_ERR_WORKSPACE:
         base = "workspace is NULL, not 16-byte aligned, or smaller than required";
+        break;
+    case FA_ERR_ALIGN:
+        base = "q, k, v, o, acc or the trace is not 16-byte aligned, or lse, m or l not 4-byte";
         break;
     default: base = "unknown status code"; break;
     }

@@ -85,7 +85,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_strerror_covers_every_code(lib):
-    for code in range(0, -12, -1):
+    for code in range(0, -13, -1):
         s = fa.fa_strerror(code)
         assert s and s != "unknown status code", code
     assert fa.fa_strerror(-99) == "unknown status code"
@@ -120,6 +120,9 @@ def _call(q=FAKE, k=FAKE2, v=FAKE3, o=FAKE4, lse=FAKE5, B=1, H=1, Nq=8, Nk=8, d=
     (dict(mask=FAKE4 + 1), fa.FA_ERR_ALIAS),
     (dict(trace=0x90000000, tb=1), fa.FA_ERR_ARG), (dict(trace=0x90000000, th=-1), fa.FA_ERR_ARG),
     (dict(trace=0x90000000, trow=8), fa.FA_ERR_ARG), (dict(trace=FAKE4 + 8), fa.FA_ERR_ALIAS),
+    (dict(q=FAKE + 8), fa.FA_ERR_ALIGN), (dict(k=FAKE2 + 2), fa.FA_ERR_ALIGN),
+    (dict(v=FAKE3 + 4), fa.FA_ERR_ALIGN), (dict(o=FAKE4 + 8), fa.FA_ERR_ALIGN),
+    (dict(lse=FAKE5 + 2), fa.FA_ERR_ALIGN), (dict(trace=0x90000008), fa.FA_ERR_ALIGN),
 ])
 def test_argument_errors_before_any_device_work(lib, kw, code):
     assert _call(**kw) == code
@@ -178,6 +181,8 @@ def _merge(m=FAKE, l=FAKE2, acc=FAKE3, n=4, rows=10, d=64, scale=0.5, o=FAKE4, l
     (dict(scale=float("nan")), fa.FA_ERR_SCALE), (dict(n=0), fa.FA_ERR_ARG),
     (dict(o=FAKE2 + 64), fa.FA_ERR_ALIAS), (dict(lse=FAKE3 + 4), fa.FA_ERR_ALIAS),
     (dict(lse=FAKE4 + 64), fa.FA_ERR_ALIAS),
+    (dict(acc=FAKE3 + 4), fa.FA_ERR_ALIGN), (dict(o=FAKE4 + 8), fa.FA_ERR_ALIGN),
+    (dict(m=FAKE + 2), fa.FA_ERR_ALIGN), (dict(lse=FAKE5 + 1), fa.FA_ERR_ALIGN),
 ])
 def test_merge_argument_errors(lib, kw, code):
     assert _merge(**kw) == code
@@ -193,6 +198,8 @@ def _softmax(s=FAKE, p=FAKE2, m=FAKE3, l=FAKE4, rows=10, n=100, dt=0):
     (dict(dt=5), fa.FA_ERR_DTYPE), (dict(p=FAKE + 4), fa.FA_ERR_ALIAS),
     (dict(m=FAKE + 40), fa.FA_ERR_ALIAS), (dict(l=FAKE2 + 8), fa.FA_ERR_ALIAS),
     (dict(l=FAKE3 + 4), fa.FA_ERR_ALIAS),
+    (dict(s=FAKE + 2), fa.FA_ERR_ALIGN), (dict(s=FAKE + 1, dt=1), fa.FA_ERR_ALIGN),
+    (dict(p=FAKE2 + 6), fa.FA_ERR_ALIGN), (dict(m=FAKE3 + 2), fa.FA_ERR_ALIGN),
 ])
 def test_softmax_argument_errors(lib, kw, code):
     assert _softmax(**kw) == code
