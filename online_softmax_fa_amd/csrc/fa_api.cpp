@@ -57,6 +57,9 @@ struct Sizes {
 };
 
 // Checks shared by the forward entry points, in the documented order.
+// The decoding pass addresses a head's K and V with 32-bit byte offsets.
+bool decode_fits(int N_k, int d) { return (int64_t)N_k * d * 2 < ((int64_t)1 << 31); }
+
 bool misaligned(const void *ptr, uintptr_t bytes)
 {
     return (reinterpret_cast<uintptr_t>(ptr) & (bytes - 1)) != 0;
@@ -178,6 +181,12 @@ int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, i
 
     fa::Params p = make_params(q, k, v, o, lse, H, N_q, N_k, scale, kv_len_mask);
     p.reverse = (opts && opts->reverse_kv) ? 1 : 0;
+    // One query row per (batch, head) in bf16, with the library's tile and
+    // order and no trace: the decoding pass, all keys in one workgroup.
+    if (dtype == FA_DTYPE_BF16 && N_q == 1 && !trace && !p.reverse &&
+        (!opts || opts->block_n == 0) && decode_fits(N_k, d))
+        return launch_status(fa::launch_decode(p, d, causal ? 1 : 0, B, H,
+                                               static_cast<hipStream_t>(stream)));
     if (trace) {
         p.trace = trace;
         p.trace_bh = opts->trace_b * H + opts->trace_h;
@@ -283,7 +292,7 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
     // One query row per (batch, head) in bf16: the decoding pass, which streams
     // K and V through registers (its offsets within a head are 32-bit);
     // otherwise the forward kernel in split mode.
-    if (dtype == FA_DTYPE_BF16 && N_q == 1 && (int64_t)N_k * d * 2 < ((int64_t)1 << 31))
+    if (dtype == FA_DTYPE_BF16 && N_q == 1 && decode_fits(N_k, d))
         rc = launch_status(fa::launch_decode(p, d, causal ? 1 : 0, B, H, st));
     else
         rc = launch_status(fa::launch_fwd(p, dtype, d, kSplitBlockN, causal ? 1 : 0, B, H, st));

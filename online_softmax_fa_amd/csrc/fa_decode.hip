@@ -280,7 +280,9 @@ __global__ __launch_bounds__(256, 2) void fa_decode_bf16_kernel(const Params p)
     }
     __syncthreads();
 
-    // Merge the waves' states into the workgroup's partial state.
+    // Merge the waves' states: the workgroup's partial state, or, without a
+    // split (all keys in this workgroup), o = o~ / l and lse = m + ln l
+    // directly (o = 0 and lse = -inf when no key was visible).
     if (threadIdx.x < D) {
         float big = kNegInf;
 #pragma unroll
@@ -293,11 +295,19 @@ __global__ __launch_bounds__(256, 2) void fa_decode_bf16_kernel(const Params p)
             l = __builtin_fmaf(f, sl[i], l);
             acc = __builtin_fmaf(f, so[i][threadIdx.x], acc);
         }
-        const size_t row = (size_t)split * p.part_rows + bh;
-        p.part_o[row * D + threadIdx.x] = acc;
-        if (threadIdx.x == 0) {
-            p.part_m[row] = big;
-            p.part_l[row] = l;
+        if (p.part_o) {
+            const size_t row = (size_t)split * p.part_rows + bh;
+            p.part_o[row * D + threadIdx.x] = acc;
+            if (threadIdx.x == 0) {
+                p.part_m[row] = big;
+                p.part_l[row] = l;
+            }
+        } else {
+            const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+            static_cast<__bf16 *>(p.o)[(size_t)bh * D + threadIdx.x] = (__bf16)(acc * inv);
+            if (threadIdx.x == 0)
+                p.lse[bh] = l > 0.0f ? __builtin_fmaf(big, p.scale, __builtin_amdgcn_logf(l) * kLn2)
+                                     : kNegInf;
         }
     }
 }

@@ -48,9 +48,10 @@ int query_tile_rows(int dtype, int d, int block_n, int B, int H, int n_q, int ca
 hipError_t launch_fwd(const Params &p, int dtype, int d, int block_n, int causal, int B, int H,
                       hipStream_t stream);
 
-// Enqueues the split-key partial pass for N_q = 1 and bf16 (decoding): the
-// workgroup of (b, h, split) writes the partial state of row b*H + h over its
-// key range, as the forward kernel does in split-key mode.
+// Enqueues the pass for N_q = 1 and bf16 (decoding): the workgroup of
+// (b, h, split) writes the partial state of row b*H + h over its key range,
+// as the forward kernel does in split-key mode, or, with n_split = 1 and no
+// partial-state buffers, o and lse of the row.
 hipError_t launch_decode(const Params &p, int d, int causal, int B, int H, hipStream_t stream);
 
 // Enqueues the merge of n_parts partial states per row (part-major layout of

@@ -290,6 +290,25 @@ def test_mask_spans(dtype, d, causal):
                 dtype, what="spans split %d" % ns)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Nk", [1, 63, 5000])
+@pytest.mark.parametrize("causal", [False, True])
+def test_single_query_row(d, Nk, causal):
+    """fa_fwd with one query row per (batch, head) in bf16 and the library's
+    tile (the decoding pass, all keys in one workgroup), with per-batch key
+    lengths and a batch whose keys are all masked."""
+    B, H = 3, 2
+    q, k, v = inputs.gaussian_qkv(B, H, 1, Nk, d, 5900 + Nk + d, 1.0, "bf16")
+    mask = inputs.prefix_mask(inputs.kv_lengths(B, Nk, 5950 + Nk, lo=1), Nk)
+    mask[1] = 0
+    scale = inputs.default_scale(d)
+    say("single query row d=%d Nk=%d causal=%d" % (d, Nk, causal))
+    o, lse = run_gpu(q, k, v, scale, causal=causal, mask=mask)
+    o_ref, lse_ref = run_oracle(q, k, v, scale, causal=causal, mask=mask)
+    compare(o, lse, o_ref, lse_ref, "bf16", what="single row")
+    assert np.all(o[1] == 0) and np.all(np.isneginf(lse[1]))
+
+
 def test_fully_masked_batch_and_rows():
     B, H, N, d = 3, 2, 96, 64
     q, k, v = inputs.gaussian_qkv(B, H, N, N, d, 77, 1.0, "bf16")
