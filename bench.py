@@ -458,6 +458,11 @@ def main():
         result["effective_tflops"] = round(4.0 * d * vis / (ms * 1e-3) / 1e12, 3)
         log("effective: %.1f TFLOP/s over the visible (query, key) pairs" %
             result["effective_tflops"])
+        if not split:
+            # the kernel's algorithmic work is the visible pairs' products
+            eff = result["effective_tflops"]
+            result["roofline"]["achieved"] = eff
+            result["roofline"]["frac"] = round(eff / peak, 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of rows ...")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
