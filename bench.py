@@ -13,6 +13,9 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
   roofline   the kernel against the bf16 dense MFMA peak (2.5 PFLOP/s)
   launch_ms  median and minimum of 20 steps timed one by one, after the
              timed region (`value` and ms_per_step are the mean of the K)
+  counters   matrix-core busy %, vector issue %, LDS bank conflicts and HBM
+             GB/s of the kernel, from the committed rocprofv3 summary
+             (profiles/), while it matches the kernel source; else null
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
              workload's rows, on this host's cores, in the same unit
 
@@ -129,6 +132,21 @@ def traffic_from_profile(workload):
     if t.get("kernel_source_sha256_16") != kernel_source_hash(workload):
         return None
     return t.get("bytes_per_launch")
+
+
+def counters_from_profile(workload):
+    """Hardware counters of the dominant kernel from the committed rocprofv3
+    summary (matrix-core busy %, vector issue %, LDS bank conflicts, HBM
+    GB/s), if they were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "%s_counters.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("kernel_source_sha256_16") != kernel_source_hash(workload):
+        return None
+    return {k: t[k] for k in ("mfma_busy_pct", "valu_issue_pct", "lds_bank_conflicts",
+                              "exp2_per_mfma", "hbm_gb_per_s") if k in t}
 
 
 def cpu_baseline(w, seconds):
@@ -447,6 +465,7 @@ def main():
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
         },
+        "counters": counters_from_profile(args.workload),
         "cpu_baseline": None,
     }
     if split:
