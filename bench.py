@@ -334,7 +334,7 @@ def main():
 
     if args.gpus != 1:
         print("bench.py measures one GPU: the attention kernel runs on a single MI355X and this "
-              "build has no multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
+              "library has no multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import torch
