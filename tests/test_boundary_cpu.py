@@ -248,3 +248,12 @@ def test_every_kernel_has_its_host_stub():
     assert len(merge) == 4, merge
     sm = [l for l in out.splitlines() if "__device_stub__fa_softmax_rows_kernel<" in l]
     assert len(sm) == 6, sm
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asking for more exits with status 2 and says
+    so, before touching any device."""
+    r = subprocess.run([os.environ.get("PYTHON", "python3"), os.path.join(ROOT, "bench.py"),
+                        "--gpus", "2"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
