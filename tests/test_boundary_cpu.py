@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -253,7 +254,7 @@ def test_every_kernel_has_its_host_stub():
 def test_bench_refuses_more_than_one_gpu():
     """bench.py measures one GPU; asking for more exits with status 2 and says
     so, before touching any device."""
-    r = subprocess.run([os.environ.get("PYTHON", "python3"), os.path.join(ROOT, "bench.py"),
-                        "--gpus", "2"], capture_output=True, text=True, timeout=120)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
