@@ -129,3 +129,25 @@ def test_graph_softmax_rows():
     for r in (0, 151, rows - 1):
         ref, _, _ = oracle.softmax_row(sets[REPLAYS][r].numpy().astype(np.float64))
         assert np.max(np.abs(got[r] - ref)) <= 1e-6
+
+
+def test_calls_run_on_the_callers_stream():
+    """Every entry point enqueues on the stream it is given (torch's current
+    stream for the binding): work on a side stream, ordered after the inputs
+    are written there and before the outputs are read there, gives the same
+    bits as on the default stream."""
+    B, H, N, d = 1, 2, 777, 128
+    q, k, v = inputs.gaussian_qkv(B, H, N, N, d, 6400, 1.0, "bf16")
+    scale = inputs.default_scale(d)
+    qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+    o0, l0 = fa.attention(qd, kd, vd, scale=scale, causal=True)
+    s0, _ = fa.attention_splitkv(qd[:, :, :1].contiguous(), kd, vd, scale=scale, num_splits=5)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        q2, k2, v2 = (x.to(DEV, non_blocking=False) for x in (q, k, v))
+        o1, l1 = fa.attention(q2, k2, v2, scale=scale, causal=True)
+        s1, _ = fa.attention_splitkv(q2[:, :, :1].contiguous(), k2, v2, scale=scale, num_splits=5)
+        got = (o1.clone(), l1.clone(), s1.clone())
+    side.synchronize()
+    assert torch.equal(got[0], o0) and torch.equal(got[1], l0) and torch.equal(got[2], s0)
