@@ -201,6 +201,7 @@ struct Bf16Fwd {
     int dmav[C::DMA_PER_WAVE];     // within a tile (row-major K / V rows)
 
     float mc, l_part;   // exponent base fl(m_ref * c) (log2 units), this lane's share of l
+    bool started;       // a key tile has been through the recurrence (wave-uniform)
     f32x16 o[D / 32];
     uint64_t kv_lo, kv_hi;
     int mnext0, mnext1;     // key-padding bytes of the next tile
@@ -297,6 +298,7 @@ struct Bf16Fwd {
 
         mc = kNegInf;
         l_part = 0.0f;
+        started = false;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -505,30 +507,36 @@ struct Bf16Fwd {
         // is and alpha is 1.  Otherwise (a score far above the base, or a row
         // with no base yet, whose weights come out +inf or NaN and fail the
         // test) the scores are formed again from the K tile, which is still
-        // in LDS, and the step with the maximum runs.
-        float fs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        // in LDS, and the step with the maximum runs.  The wave's first tile
+        // has no base in any row, so it goes to that step directly.
+        float tot = 0.0f;
+        bool done = false;
+        if (started) {
+            float fs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
+            for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                s[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
-                fs[r & 3] += s[kb][r];
-            }
-        const float tot = (fs[0] + fs[1]) + (fs[2] + fs[3]);
-        const bool done = !__any(!(tot <= 65536.0f));
-        // the V reads first, then the vector work
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * VA, 9);
-        __builtin_amdgcn_sched_group_barrier(0x406, 512, 9);
+                for (int r = 0; r < 16; ++r) {
+                    s[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
+                    fs[r & 3] += s[kb][r];
+                }
+            tot = (fs[0] + fs[1]) + (fs[2] + fs[3]);
+            done = !__any(!(tot <= 65536.0f));
+            // the V reads first, then the vector work
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * VA, 9);
+            __builtin_amdgcn_sched_group_barrier(0x406, 512, 9);
+        }
         if (done) {
 #pragma unroll
             for (int t16 = 0; t16 < C::NT16; ++t16)
 #pragma unroll
                 for (int i = 0; i < 8; ++i) pb[t16][i] = (__bf16)s[t16 >> 1][8 * (t16 & 1) + i];
             l_part += tot;
-        } else {
+        } else if (started) {
             qk<ST>(s);
             mask_scores(k0, s);
         }
+        started = true;
         float alpha;
         if (!done && lazy_step<C::NKB, C::NT16>(s, pb, mc, l_part, c, alpha)) {
 #pragma unroll
