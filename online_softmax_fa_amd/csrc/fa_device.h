@@ -110,7 +110,7 @@ __device__ __forceinline__ float pair_sum(float x)
 // The exponent base mc = fl(m_ref * c) (log2 units) follows the running
 // maximum, but moves only when a step's maximum exceeds it by more than
 // kLag.  Until then the weights exp2(s*c - mc) may exceed 1, up to
-// 2^kLag = 256 here and 2^16 on the kernels' fast path that skips this step
+// 2^kLag = 256 here and 2^24 on the kernels' fast path that skips this step
 // -- far from any fp32 or bf16 limit -- and alpha is exactly 1,
 // so the rescale of o~ is skipped; when the base does move,
 // alpha = exp2(mc_old - mc_new) < 2^-kLag rescales l and o~ as the pages'
@@ -118,7 +118,7 @@ __device__ __forceinline__ float pair_sum(float x)
 // o~ / l and lse = (mc + log2 l) ln 2 are the same quantities as with the
 // exact running maximum ("2.2b", "Why This Algorithm is Exact": any common
 // reference cancels; "The math of FlashAttention", "Proof of numerical
-// stability": here every exponent is at most 16 instead of 0).
+// stability": here every exponent is at most 24 instead of 0).
 //
 // s: raw scores in (hidden keys at -inf), fp32 weights out; l_part: this
 // lane's share of l, summed over the fp32 weights.  Returns whether o~ must

@@ -503,7 +503,7 @@ struct Bf16Fwd {
         bf16x8 pb[C::NT16];
         // Fast path: the weights against the current base, without the tile
         // maximum.  They are kept when every lane's sum of them is at most
-        // 2^16, which bounds each weight by 2^16 too; the base stays where it
+        // 2^24, which bounds each weight by 2^24 too; the base stays where it
         // is and alpha is 1.  Otherwise (a score far above the base, or a row
         // with no base yet, whose weights come out +inf or NaN and fail the
         // test) the scores are formed again from the K tile, which is still
@@ -521,7 +521,7 @@ struct Bf16Fwd {
                     fs[r & 3] += s[kb][r];
                 }
             tot = (fs[0] + fs[1]) + (fs[2] + fs[3]);
-            done = !__any(!(tot <= 65536.0f));
+            done = !__any(!(tot <= 16777216.0f));
             // the V reads first, then the vector work
             __builtin_amdgcn_sched_group_barrier(0x100, 2 * VA, 9);
             __builtin_amdgcn_sched_group_barrier(0x406, 512, 9);

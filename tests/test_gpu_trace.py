@@ -118,7 +118,8 @@ def test_trace_of_adversarial_rows(dtype, bn, rev):
                         m_true = e["m_new"] / scale
                         slack = 1e-6 * abs(m_true) + 1e-6         # rounding of mc / c
                         assert m <= m_true + slack
-                        assert m >= m_true - 16.0 / c - slack
+                        # lag bound: the fast path keeps weights up to 2^24
+                        assert m >= m_true - 24.0 / c - slack
                     assert abs(lse_k - lse_o) <= 1e-5 * max(1.0, abs(lse_o))
 
 
