@@ -67,10 +67,12 @@ typedef enum fa_status {
     FA_ERR_ARG = -10,      /* another argument is out of range: the traced row,
                               num_splits, n_parts                                */
     FA_ERR_WORKSPACE = -11,/* workspace NULL or smaller than required            */
-    FA_ERR_ALIGN = -12     /* a pointer is not aligned as its entry point needs:
+    FA_ERR_ALIGN = -12,    /* a pointer is not aligned as its entry point needs:
                               16 bytes for q, k, v, o, acc and the trace, 4 bytes
                               for lse, m and l, the element size for the score
                               rows s and p of fa_softmax_rows                    */
+    FA_ERR_SCRATCH = -13   /* the partial states of fa_fwd_splitkv_noalloc would
+                              not fit the library's device scratch (32 MiB)      */
 } fa_status;
 
 typedef enum fa_dtype {
@@ -248,6 +250,34 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
                    int B, int H, int N_q, int N_k, int d, float scale, int causal,
                    const uint8_t *kv_len_mask, int dtype, int num_splits,
                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * fa_fwd_splitkv_noalloc -- fa_fwd_splitkv for callers that cannot allocate
+ * device memory or pass a workspace: code recorded under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * checks and result as fa_fwd_splitkv, without workspace and
+ * workspace_bytes: the partial states go to a scratch array owned by the
+ * library instead.
+ *
+ *   scratch      32 MiB of device memory per GPU, a static array of the
+ *                library that each GPU it runs on holds until the process
+ *                ends.  A call needs fa_splitkv_workspace_bytes(B, H, N_q, d,
+ *                num_splits) bytes of it; more gives FA_ERR_SCRATCH before
+ *                anything is enqueued.  The first call on a device looks the
+ *                array's address up (no allocation); later calls reuse it.
+ *   allocation   none: no hipMalloc, hipFree or allocating library routine
+ *                on any call.
+ *   sharing      every call on one GPU uses the same array, which keeps the
+ *                last call's partial states.  Nothing in it needs to start at
+ *                zero (every part of every row is written before it is read),
+ *                but two calls that overlap in time on one GPU -- on
+ *                different streams, or from different host threads without
+ *                ordering -- race on it and give undefined results.
+ */
+int fa_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                           int B, int H, int N_q, int N_k, int d, float scale, int causal,
+                           const uint8_t *kv_len_mask, int dtype, int num_splits,
+                           void *stream);
 
 /*
  * fa_merge_states -- merge n_parts partial states per row (layout above) into

@@ -12,6 +12,7 @@ Entry points (same names and meaning as include/fa.h):
   fa_splitkv_workspace_bytes(B, H, N_q, d, num_splits)
   fa_splitkv_splits(B, H, N_q, N_k, d, causal)
   fa_fwd_splitkv(..., dtype, num_splits, workspace, workspace_bytes, stream)
+  fa_fwd_splitkv_noalloc(..., dtype, num_splits, stream)
   fa_merge_states(m, l, acc, n_parts, rows, d, scale, o, lse, dtype, stream)
   fa_softmax_rows(s, p, m, l, rows, n, dtype, stream)
   fa_strerror(code)
@@ -43,6 +44,7 @@ FA_ERR_ALIAS = -9
 FA_ERR_ARG = -10
 FA_ERR_WORKSPACE = -11
 FA_ERR_ALIGN = -12
+FA_ERR_SCRATCH = -13
 
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
@@ -89,6 +91,9 @@ def load_library(path=LIB_PATH):
     lib.fa_fwd_splitkv.restype = ci
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, vp, ci, ci, vp,
                                    sz, vp]
+    lib.fa_fwd_splitkv_noalloc.restype = ci
+    lib.fa_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, vp, ci,
+                                           ci, vp]
     lib.fa_merge_states.restype = ci
     lib.fa_merge_states.argtypes = [vp, vp, vp, ci, i64, ci, cf, vp, vp, ci, vp]
     lib.fa_softmax_rows.restype = ci
@@ -162,6 +167,17 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, H, N_q, N_k, d, scale, causal, kv_len_mas
                                        N_k, d, float(scale), int(bool(causal)), _ptr(kv_len_mask),
                                        int(dtype), int(num_splits), _ptr(workspace),
                                        int(workspace_bytes), stream)
+    _check(rc)
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, N_q, N_k, d, scale, causal, kv_len_mask,
+                           dtype, num_splits, stream):
+    """C fa_fwd_splitkv_noalloc: the split-key pass with its partial states in
+    the library's own device scratch (no workspace, nothing allocated)."""
+    rc = load_library().fa_fwd_splitkv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B,
+                                               H, N_q, N_k, d, float(scale), int(bool(causal)),
+                                               _ptr(kv_len_mask), int(dtype), int(num_splits),
+                                               stream)
     _check(rc)
 
 

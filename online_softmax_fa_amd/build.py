@@ -10,7 +10,8 @@ import sys
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 SOURCES = [os.path.join(_HERE, "csrc", f)
-           for f in ("fa_kernels.hip", "fa_decode.hip", "fa_softmax.hip", "fa_api.cpp")]
+           for f in ("fa_kernels.hip", "fa_decode.hip", "fa_softmax.hip", "fa_noalloc.hip",
+                     "fa_api.cpp")]
 OUT = os.path.join(_HERE, "libfa.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

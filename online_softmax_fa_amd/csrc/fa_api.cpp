@@ -196,6 +196,62 @@ int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, i
                                         static_cast<hipStream_t>(stream)));
 }
 
+// fa_fwd_splitkv and fa_fwd_splitkv_noalloc: the partial states go to the
+// caller's workspace, or (use_scratch) to the library's own device scratch,
+// whose address is looked up once per device and which is never allocated
+// here.
+int splitkv_impl(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                 int N_q, int N_k, int d, float scale, int causal, const uint8_t *kv_len_mask,
+                 int dtype, int num_splits, void *workspace, size_t workspace_bytes,
+                 bool use_scratch, void *stream)
+{
+    Sizes sz;
+    const int ns = (num_splits >= 1 && num_splits <= kMaxSplits) ? num_splits : 1;
+    int rc = check_fwd_args(q, k, v, o, lse, B, H, N_q, N_k, d, scale, kv_len_mask, dtype, ns, sz);
+    if (rc != FA_OK) return rc;
+    if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_ARG;
+    size_t acc_off = 0, total = 0;
+    if (!splitkv_layout(sz.rows, d, num_splits, acc_off, total)) return FA_ERR_SHAPE;
+    if (use_scratch) {
+        if (total > fa::kScratchBytes) return FA_ERR_SCRATCH;
+    } else {
+        if (!workspace || workspace_bytes < total ||
+            (reinterpret_cast<uintptr_t>(workspace) & 15))
+            return FA_ERR_WORKSPACE;
+        if (overlaps_fwd(workspace, total, q, k, v, o, lse, kv_len_mask, sz)) return FA_ERR_ALIAS;
+    }
+
+    rc = check_device();
+    if (rc != FA_OK) return rc;
+    if (use_scratch) {
+        const hipError_t e = fa::scratch_address(&workspace);
+        if (e != hipSuccess) {
+            g_last_hip = e;
+            return FA_ERR_DEVICE;
+        }
+    }
+
+    fa::Params p = make_params(q, k, v, o, lse, H, N_q, N_k, scale, kv_len_mask);
+    float *ws = static_cast<float *>(workspace);
+    p.n_split = num_splits;
+    p.part_rows = sz.rows;
+    p.part_m = ws;
+    p.part_l = ws + (size_t)num_splits * sz.rows;
+    p.part_o = reinterpret_cast<float *>(static_cast<char *>(workspace) + acc_off);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    // One query row per (batch, head) in bf16: the decoding pass, which streams
+    // K and V through registers (its offsets within a head are 32-bit);
+    // otherwise the forward kernel in split mode.  Both write every part of
+    // every row, so nothing in the workspace needs clearing first.
+    if (dtype == FA_DTYPE_BF16 && N_q == 1 && decode_fits(N_k, d))
+        rc = launch_status(fa::launch_decode(p, d, causal ? 1 : 0, B, H, st));
+    else
+        rc = launch_status(fa::launch_fwd(p, dtype, d, kSplitBlockN, causal ? 1 : 0, B, H, st));
+    if (rc != FA_OK) return rc;
+    return launch_status(fa::launch_merge(p.part_m, p.part_l, p.part_o, num_splits, sz.rows, d,
+                                          scale, o, lse, dtype, st));
+}
+
 }  // namespace
 
 extern "C" {
@@ -267,38 +323,16 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
                    const uint8_t *kv_len_mask, int dtype, int num_splits, void *workspace,
                    size_t workspace_bytes, void *stream)
 {
-    Sizes sz;
-    const int ns = (num_splits >= 1 && num_splits <= kMaxSplits) ? num_splits : 1;
-    int rc = check_fwd_args(q, k, v, o, lse, B, H, N_q, N_k, d, scale, kv_len_mask, dtype, ns, sz);
-    if (rc != FA_OK) return rc;
-    if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_ARG;
-    size_t acc_off = 0, total = 0;
-    if (!splitkv_layout(sz.rows, d, num_splits, acc_off, total)) return FA_ERR_SHAPE;
-    if (!workspace || workspace_bytes < total || (reinterpret_cast<uintptr_t>(workspace) & 15))
-        return FA_ERR_WORKSPACE;
-    if (overlaps_fwd(workspace, total, q, k, v, o, lse, kv_len_mask, sz)) return FA_ERR_ALIAS;
+    return splitkv_impl(q, k, v, o, lse, B, H, N_q, N_k, d, scale, causal, kv_len_mask, dtype,
+                        num_splits, workspace, workspace_bytes, false, stream);
+}
 
-    rc = check_device();
-    if (rc != FA_OK) return rc;
-
-    fa::Params p = make_params(q, k, v, o, lse, H, N_q, N_k, scale, kv_len_mask);
-    float *ws = static_cast<float *>(workspace);
-    p.n_split = num_splits;
-    p.part_rows = sz.rows;
-    p.part_m = ws;
-    p.part_l = ws + (size_t)num_splits * sz.rows;
-    p.part_o = reinterpret_cast<float *>(static_cast<char *>(workspace) + acc_off);
-    const hipStream_t st = static_cast<hipStream_t>(stream);
-    // One query row per (batch, head) in bf16: the decoding pass, which streams
-    // K and V through registers (its offsets within a head are 32-bit);
-    // otherwise the forward kernel in split mode.
-    if (dtype == FA_DTYPE_BF16 && N_q == 1 && decode_fits(N_k, d))
-        rc = launch_status(fa::launch_decode(p, d, causal ? 1 : 0, B, H, st));
-    else
-        rc = launch_status(fa::launch_fwd(p, dtype, d, kSplitBlockN, causal ? 1 : 0, B, H, st));
-    if (rc != FA_OK) return rc;
-    return launch_status(fa::launch_merge(p.part_m, p.part_l, p.part_o, num_splits, sz.rows, d,
-                                          scale, o, lse, dtype, st));
+int fa_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                           int B, int H, int N_q, int N_k, int d, float scale, int causal,
+                           const uint8_t *kv_len_mask, int dtype, int num_splits, void *stream)
+{
+    return splitkv_impl(q, k, v, o, lse, B, H, N_q, N_k, d, scale, causal, kv_len_mask, dtype,
+                        num_splits, nullptr, 0, true, stream);
 }
 
 int fa_merge_states(const float *m, const float *l, const float *acc, int n_parts, int64_t rows,
@@ -372,6 +406,10 @@ const char *fa_strerror(int code)
         break;
     case FA_ERR_ALIGN:
         base = "q, k, v, o, acc or the trace is not 16-byte aligned, or lse, m or l not 4-byte";
+        break;
+    case FA_ERR_SCRATCH:
+        base = "the partial states exceed the library's device scratch (32 MiB per GPU); "
+               "use fa_fwd_splitkv with a workspace, or fewer splits";
         break;
     default: base = "unknown status code"; break;
     }

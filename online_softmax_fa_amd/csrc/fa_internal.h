@@ -60,6 +60,14 @@ hipError_t launch_merge(const float *m, const float *l, const float *acc, int n_
                         int64_t rows, int d, float scale, void *o, float *lse, int dtype,
                         hipStream_t stream);
 
+// Bytes of the library's own device scratch (fa_fwd_splitkv_noalloc), one
+// array per GPU, held until the process ends.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+
+// Device address of that scratch on the current device, looked up once per
+// device (hipGetSymbolAddress) and cached.
+hipError_t scratch_address(void **ptr);
+
 // Enqueues the row softmax (fa_softmax_rows) for validated arguments.
 hipError_t launch_softmax_rows(const void *s, void *p, float *m, float *l, int64_t rows,
                                int64_t n, int dtype, hipStream_t stream);

@@ -30,7 +30,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["fa_fwd", "fa_fwd_ex", "fa_fwd_splitkv", "fa_merge_states",
+    assert _declared_functions() == ["fa_fwd", "fa_fwd_ex", "fa_fwd_splitkv",
+                                     "fa_fwd_splitkv_noalloc", "fa_merge_states",
                                      "fa_query_tile_rows", "fa_softmax_rows", "fa_splitkv_splits",
                                      "fa_splitkv_workspace_bytes", "fa_strerror"]
 
@@ -86,7 +87,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_strerror_covers_every_code(lib):
-    for code in range(0, -13, -1):
+    for code in range(0, -14, -1):
         s = fa.fa_strerror(code)
         assert s and s != "unknown status code", code
     assert fa.fa_strerror(-99) == "unknown status code"
@@ -137,6 +138,7 @@ def test_valid_arguments_without_gpu_report_device_error(lib):
     assert _call(trace=0x90000000, tb=0, th=0, trow=7) == fa.FA_ERR_DEVICE
     assert _split() == fa.FA_ERR_DEVICE
     assert _merge() == fa.FA_ERR_DEVICE
+    assert _noalloc() == fa.FA_ERR_DEVICE
     assert lib.fa_splitkv_splits(1, 8, 1, 32768, 128, 0) == fa.FA_ERR_DEVICE
 
 
@@ -159,6 +161,39 @@ def _split(B=1, H=2, Nq=8, Nk=8, d=64, ns=3, ws=WS, ws_bytes=None, q=FAKE, o=FAK
 ])
 def test_splitkv_argument_errors(lib, kw, code):
     assert _split(**kw) == code
+
+
+def _noalloc(B=1, H=2, Nq=8, Nk=8, d=64, ns=3, q=FAKE, o=FAKE4, lse=FAKE5):
+    lib = fa.load_library()
+    return lib.fa_fwd_splitkv_noalloc(q, FAKE2, FAKE3, o, lse, B, H, Nq, Nk, d, 0.125, 0, None, 1,
+                                      ns, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), fa.FA_ERR_NULL), (dict(B=0), fa.FA_ERR_SHAPE), (dict(d=80), fa.FA_ERR_HEAD_DIM),
+    (dict(ns=0), fa.FA_ERR_ARG), (dict(ns=257), fa.FA_ERR_ARG), (dict(o=FAKE), fa.FA_ERR_ALIAS),
+    (dict(lse=FAKE5 + 2), fa.FA_ERR_ALIGN),
+    # partial states of 2*16*1024 rows x 16 parts x (128 + 2) floats: 272 MB > 32 MiB
+    (dict(B=2, H=16, Nq=1024, Nk=1024, d=128, ns=16), fa.FA_ERR_SCRATCH),
+])
+def test_splitkv_noalloc_argument_errors(lib, kw, code):
+    """The no-alloc split-key entry point checks what fa_fwd_splitkv checks
+    (no workspace), and rejects partial states beyond its 32 MiB scratch, all
+    before touching a device."""
+    assert _noalloc(**kw) == code
+
+
+def test_splitkv_noalloc_scratch_limit_is_the_workspace_size(lib):
+    """The largest request that fits is the one whose fa_fwd_splitkv workspace
+    is at most 32 MiB."""
+    import torch
+    limit = 32 << 20
+    d, ns = 128, 16
+    rows_max = max(r for r in range(1, 5000) if lib.fa_splitkv_workspace_bytes(1, 1, r, d, ns) <= limit)
+    assert lib.fa_splitkv_workspace_bytes(1, 1, rows_max + 1, d, ns) > limit
+    assert _noalloc(B=1, H=1, Nq=rows_max + 1, Nk=64, d=d, ns=ns) == fa.FA_ERR_SCRATCH
+    if not torch.cuda.is_available():
+        assert _noalloc(B=1, H=1, Nq=rows_max, Nk=64, d=d, ns=ns) == fa.FA_ERR_DEVICE
 
 
 def test_splitkv_workspace_bytes_follow_the_documented_layout(lib):
