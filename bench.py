@@ -18,6 +18,11 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
              (profiles/), while it matches the kernel source; else null
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
              workload's rows, on this host's cores, in the same unit
+  parity     the last launch's o and lse on those sample rows against the
+             oracle's: max-abs and mean-abs of o, max-abs of lse, the bars
+             and pass/fail
+  peak_from_device  CUs x peak engine clock x 4096 (bf16 FLOP per CU per
+             clock) as the device reports them, beside the published 2.5 PF
 
 With --workload softmax (8192 rows of 8192 fp32 scores) a step is one
 fa_softmax_rows call, reported as HBM GB/s of its compulsory bytes (the rows
@@ -146,7 +151,7 @@ def counters_from_profile(workload):
     if t.get("kernel_source_sha256_16") != kernel_source_hash(workload):
         return None
     return {k: t[k] for k in ("mfma_busy_pct", "valu_issue_pct", "lds_bank_conflicts",
-                              "exp2_per_mfma", "hbm_gb_per_s") if k in t}
+                              "exp2_per_mfma", "hbm_gb_per_s", "sustained_clock_ghz") if k in t}
 
 
 def cpu_baseline(w, seconds):
@@ -175,18 +180,18 @@ def cpu_baseline(w, seconds):
     def timed(nrows):
         rows = np.linspace(0, total_rows - 1, nrows).astype(np.int64)
         t0 = time.perf_counter()
-        _, _, used = oracle.attn_fwd(q, k, v, w["scale"], causal=w["causal"], mask=mask,
-                                     rows=rows, threads=threads)
-        return time.perf_counter() - t0, row_flops(rows), used
+        o_ref, lse_ref, used = oracle.attn_fwd(q, k, v, w["scale"], causal=w["causal"],
+                                               mask=mask, rows=rows, threads=threads)
+        return time.perf_counter() - t0, row_flops(rows), used, (rows, o_ref, lse_ref)
 
     n = max(threads, 16)
-    dt, fl, used = timed(n)
+    dt, fl, used, ref = timed(n)
     while dt < 1.0 and n < total_rows:
         n = min(total_rows, n * 4)
-        dt, fl, used = timed(n)
+        dt, fl, used, ref = timed(n)
     if dt < seconds and n < total_rows:
         n = int(min(total_rows, n * seconds / max(dt, 1e-3)))
-        dt, fl, used = timed(n)
+        dt, fl, used, ref = timed(n)
     # the metric's flop count counts a causal run as half of the full square
     return {
         "value": fl / dt / (1e9 if hbm else 1e12),
@@ -196,7 +201,65 @@ def cpu_baseline(w, seconds):
         "cpu": cpu_model(),
         "sample": "%d of %d query rows (evenly spaced over all heads), fp64 three-pass "
                   "oracle, %.1f s wall" % (n, total_rows, dt),
-    }
+    }, ref
+
+
+# Parity bars: O max-abs (and mean-abs for bf16) against the fp64 oracle, lse
+# max-abs; rows with no visible key must be exactly o = 0, lse = -inf.
+PARITY_BARS = {"f32": {"max_abs": 1e-5, "mean_abs": None, "lse_max_abs": 1e-3},
+               "bf16": {"max_abs": 2e-2, "mean_abs": 2e-3, "lse_max_abs": 1e-3}}
+
+
+def parity(o, lse, ref, dtype):
+    """The GPU's o and lse (of the last launch, same inputs) on the oracle's
+    sample rows against the oracle's fp64 values."""
+    import numpy as np
+    import torch
+    rows, o_ref, lse_ref = ref
+    d = o.shape[-1]
+    idx = torch.from_numpy(rows).to(o.device)
+    og = o.reshape(-1, d)[idx].float().cpu().numpy().astype(np.float64)
+    lg = lse.reshape(-1)[idx].cpu().numpy().astype(np.float64)
+    o_ref = o_ref.reshape(-1, d)
+    dead = np.isneginf(lse_ref)
+    live = ~dead
+    bars = PARITY_BARS[dtype]
+    out = {"rows": int(len(rows)), "rows_without_visible_key": int(dead.sum()),
+           "bars": bars}
+    ok = bool(np.all(og[dead] == 0.0) and np.all(np.isneginf(lg[dead])) and
+              np.all(np.isfinite(og)) and np.all(np.isfinite(lg[live])))
+    if live.any():
+        err = np.abs(og[live] - o_ref[live])
+        out["max_abs"] = float(err.max())
+        out["mean_abs"] = float(err.mean())
+        out["lse_max_abs"] = float(np.abs(lg[live] - lse_ref[live]).max())
+        ok = ok and out["max_abs"] <= bars["max_abs"] and out["lse_max_abs"] <= bars["lse_max_abs"]
+        if bars["mean_abs"] is not None:
+            ok = ok and out["mean_abs"] <= bars["mean_abs"]
+    out["pass"] = ok
+    return out
+
+
+def device_peak(torch, dev):
+    """CUs x peak engine clock x 4096 bf16 FLOP per CU per clock (gfx950
+    dense MFMA), from the device the bench runs on (HIP runtime attributes,
+    through the runtime torch has loaded)."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+    except OSError:
+        hip = ctypes.CDLL("libamdhip64.so")
+    val = ctypes.c_int(0)
+    idx = dev.index or 0
+
+    def attr(a):    # hipDeviceAttributeClockRate = 5 (kHz), MultiprocessorCount = 63
+        return val.value if hip.hipDeviceGetAttribute(ctypes.byref(val), a, idx) == 0 else 0
+
+    khz, cus = attr(5), attr(63)
+    if khz <= 0 or cus <= 0:
+        return None
+    return {"cus": cus, "clock_mhz": round(khz / 1e3, 1),
+            "tflops": round(cus * khz * 1e3 * 4096 / 1e12, 1)}
 
 
 def cpu_tiled(w, seconds):
@@ -424,11 +487,10 @@ def main():
         else:
             metric = "attention fwd TFLOP/s and %% of %s MFMA peak, 1 MI355X, N=%d d=%d %s" % (
                 w["dtype"], N, d, "causal" if w["causal"] else "non-causal")
-        clk = getattr(props, "clock_rate", 0) or 0     # kHz, as the runtime reports it
-        if clk:
+        dpeak = device_peak(torch, dev)
+        if dpeak:
             log("bf16 dense peak from the device: %d CUs x %.0f MHz x 4096 FLOP/clk = %.1f "
-                "TFLOP/s (published: 2500)" % (props.multi_processor_count, clk / 1e3,
-                                               props.multi_processor_count * clk * 1e3 * 4096 / 1e12))
+                "TFLOP/s (published: 2500)" % (dpeak["cus"], dpeak["clock_mhz"], dpeak["tflops"]))
         log("%.1f TFLOP/s = %.1f%% of %.0f TFLOP/s (%s, %d CUs)" % (
             tflops, 100 * tflops / peak, peak, props.name, props.multi_processor_count))
 
@@ -467,7 +529,15 @@ def main():
         },
         "counters": counters_from_profile(args.workload),
         "cpu_baseline": None,
+        "parity": None,
     }
+    if not split:
+        result["peak_from_device"] = dpeak
+        cnt = result["counters"] or {}
+        if "sustained_clock_ghz" in cnt and dpeak:
+            # the matrix-core ceiling at the clock the chip held under this load
+            result["peak_at_sustained_clock"] = round(
+                dpeak["cus"] * cnt["sustained_clock_ghz"] * 1e9 * 4096 / 1e12, 1)
     if split:
         result["config"]["splits"] = ns
     if lens is not None:
@@ -484,8 +554,11 @@ def main():
             result["roofline"]["frac"] = round(eff / peak, 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of rows ...")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        result["cpu_baseline"], ref = cpu_baseline(w, args.cpu_seconds)
         log("cpu baseline: %s" % result["cpu_baseline"])
+        # the oracle's rows are the parity check of the last launch's output
+        result["parity"] = parity(o, lse, ref, w["dtype"])
+        log("parity against the fp64 oracle: %s" % result["parity"])
         log("timing the host-CPU tiled implementation on whole heads ...")
         result["cpu_tiled"] = cpu_tiled(w, args.cpu_seconds / 3)
         log("cpu tiled: %s" % result["cpu_tiled"])

@@ -121,6 +121,23 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
            const uint8_t *kv_len_mask, int dtype, void *stream);
 
 /*
+ * FA_BF16_REF_LAG_LOG2 -- how far (in log2 units of the scaled scores) the
+ * bfloat16 kernels let their exponent reference lag a row's running maximum.
+ * A tile keeps the current reference when every weight exp2(score * scale *
+ * log2 e - reference) stays within 2^FA_BF16_REF_LAG_LOG2; a larger score
+ * moves the reference up to it.  Any common reference cancels in o~ / l and in
+ * lse ("2.2b: FlashAttention -- Online Softmax", "Why This Algorithm is
+ * Exact"), so the results are those of the running maximum; the cost is
+ * headroom: o~ and l carry up to 2^FA_BF16_REF_LAG_LOG2 times the magnitudes
+ * of the pages' recurrence, whose weights are at most 1 ("The math of
+ * FlashAttention", "Proof of numerical stability").  With float32
+ * accumulators that leaves about 2^(128 - 24) for |v| times the number of
+ * keys -- far beyond any bfloat16 input -- but it is 24 bits less than the
+ * pages' bound.  The float32 kernels keep the exact running maximum.
+ */
+#define FA_BF16_REF_LAG_LOG2 24
+
+/*
  * Test hooks.  A zeroed struct (or a NULL pointer) gives fa_fwd's behaviour.
  *
  *   block_n     keys per tile of the recurrence: 0 (library choice, 64), 16,
@@ -143,8 +160,9 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  *               over the keys absorbed so far (-inf and 0 while none is
  *               visible).  For float32, m is the running maximum itself.  For
  *               bfloat16, m lags it: the kernel moves its reference only when
- *               a tile's scores exceed it by more than 16 / (scale * log2 e),
- *               so running max - that bound <= m <= running max.  Tiles the
+ *               a tile's scores exceed it by more than
+ *               FA_BF16_REF_LAG_LOG2 / (scale * log2 e), so running max -
+ *               that bound <= m <= running max.  Tiles the
  *               kernel never visits leave their entries untouched: those
  *               above the causal diagonal of the row's query tile
  *               (fa_query_tile_rows rows) and, with kv_len_mask, those
@@ -180,7 +198,9 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
  * a workgroup visits the key tiles up to the diagonal of the last row of its
  * query tile, so a trace has one entry per such tile.  Returns the row
  * count, or FA_ERR_SHAPE (B, H or N_q < 1) / FA_ERR_HEAD_DIM / FA_ERR_DTYPE /
- * FA_ERR_TILE.  Pure function of its arguments: no device call.
+ * FA_ERR_TILE.  Besides its arguments it depends only on the current
+ * device's compute-unit count ("enough workgroups"), queried once per device;
+ * without a usable device it assumes the MI355X's 256.  It enqueues nothing.
  */
 int fa_query_tile_rows(int dtype, int B, int H, int N_q, int d, int block_n, int causal);
 

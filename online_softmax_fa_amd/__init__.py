@@ -207,7 +207,11 @@ def softmax_rows(s, out=None):
         raise FaError(FA_ERR_SHAPE, "s must be a contiguous GPU tensor")
     n = s.shape[-1]
     rows = s.numel() // n if n else 0
-    p = torch.empty_like(s) if out is None else out
+    if out is None:
+        p = torch.empty_like(s)
+    else:
+        _check_out("out", out, s.shape, s.dtype, s.device)
+        p = out
     m = torch.empty(s.shape[:-1], dtype=torch.float32, device=s.device)
     l = torch.empty(s.shape[:-1], dtype=torch.float32, device=s.device)
     stream = torch.cuda.current_stream(s.device).cuda_stream
@@ -241,11 +245,28 @@ def _check_qkv(q, k, v, kv_len_mask):
     return dt, B, H, Nq, Nk, d
 
 
+def _check_out(name, t, shape, dtype, device):
+    """A caller-supplied output must be exactly what the kernels write: the C
+    layer sees only a pointer, so a smaller or differently typed buffer would
+    be written past its end."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise FaError(FA_ERR_SHAPE, "%s must be a torch tensor" % name)
+    if t.dtype != dtype or t.device != device or not t.is_contiguous() or \
+            tuple(t.shape) != tuple(shape):
+        raise FaError(FA_ERR_SHAPE, "%s must be a contiguous %s tensor of shape %s on %s (got %s "
+                      "%s%s on %s)" % (name, dtype, tuple(shape), device, t.dtype, tuple(t.shape),
+                                       "" if t.is_contiguous() else ", not contiguous", t.device))
+
+
 def _outputs(q, out):
     import torch
-    if out is not None:
-        return out
     B, H, Nq, _ = q.shape
+    if out is not None:
+        o, lse = out
+        _check_out("o", o, q.shape, q.dtype, q.device)
+        _check_out("lse", lse, (B, H, Nq), torch.float32, q.device)
+        return o, lse
     return torch.empty_like(q), torch.empty(B, H, Nq, dtype=torch.float32, device=q.device)
 
 
@@ -266,6 +287,9 @@ def attention_splitkv(q, k, v, scale=None, causal=False, kv_len_mask=None, num_s
         raise FaError(FA_ERR_ARG, "num_splits must be in 1..256")
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    elif (not isinstance(workspace, torch.Tensor) or workspace.device != q.device
+          or not workspace.is_contiguous()):
+        raise FaError(FA_ERR_WORKSPACE, "workspace must be a contiguous tensor on %s" % q.device)
     o, lse = _outputs(q, out)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     fa_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_len_mask, dt, num_splits,
@@ -290,6 +314,8 @@ def merge_states(m, l, acc, scale, out_dtype=None, out=None):
         lse = torch.empty(rows, dtype=torch.float32, device=acc.device)
     else:
         o, lse = out
+        _check_out("o", o, (rows, d), o.dtype, acc.device)
+        _check_out("lse", lse, (rows,), torch.float32, acc.device)
     dt = _dtype_code(o)
     stream = torch.cuda.current_stream(acc.device).cuda_stream
     fa_merge_states(m, l, acc, n_parts, rows, d, scale, o, lse, dt, stream)

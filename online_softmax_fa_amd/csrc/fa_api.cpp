@@ -43,6 +43,10 @@ int check_device()
     return kind == 1 ? FA_OK : FA_ERR_DEVICE;
 }
 
+// Compute units and XCDs per device, queried once: 0 = not yet known.
+std::atomic<int> g_dev_cus[64];
+std::atomic<int> g_dev_xcds[64];
+
 bool overlaps(const void *a, size_t na, const void *b, size_t nb)
 {
     if (!a || !b || na == 0 || nb == 0) return false;
@@ -114,6 +118,7 @@ fa::Params make_params(const void *q, const void *k, const void *v, void *o, flo
 {
     fa::Params p;
     std::memset(&p, 0, sizeof p);
+    fa::device_geometry(p.cus, p.xcds);
     p.q = q;
     p.k = k;
     p.v = v;
@@ -254,6 +259,35 @@ int splitkv_impl(const void *q, const void *k, const void *v, void *o, float *ls
 
 }  // namespace
 
+namespace fa {
+
+void device_geometry(int &cus, int &xcds)
+{
+    cus = 256;
+    xcds = 8;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return;
+    int c = g_dev_cus[dev].load(std::memory_order_acquire);
+    int x = g_dev_xcds[dev].load(std::memory_order_acquire);
+    if (c == 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            c <= 0)
+            c = 256;
+        if (hipDeviceGetAttribute(&x, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || x <= 0)
+            x = 1;
+        // The grid mapping deals workgroups to XCDs in turn; an XCD count it
+        // cannot use that way (not a power of two, or not dividing the CUs
+        // evenly) falls back to the plain order of one.
+        if ((x & (x - 1)) != 0 || c % x != 0) x = 1;
+        g_dev_xcds[dev].store(x, std::memory_order_release);
+        g_dev_cus[dev].store(c, std::memory_order_release);
+    }
+    cus = c;
+    xcds = x;
+}
+
+}  // namespace fa
+
 extern "C" {
 
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
@@ -289,7 +323,10 @@ int fa_query_tile_rows(int dtype, int B, int H, int N_q, int d, int block_n, int
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
     if (block_n != 0 && block_n != 16 && block_n != 32 && block_n != 64 && block_n != 128)
         return FA_ERR_TILE;
-    return fa::query_tile_rows(dtype, d, block_n == 0 ? 64 : block_n, B, H, N_q, causal ? 1 : 0, 1);
+    int cus = 256, xcds = 8;
+    fa::device_geometry(cus, xcds);
+    return fa::query_tile_rows(dtype, d, block_n == 0 ? 64 : block_n, B, H, N_q, causal ? 1 : 0, 1,
+                               cus);
 }
 
 int fa_splitkv_splits(int B, int H, int N_q, int N_k, int d, int causal)
@@ -298,15 +335,13 @@ int fa_splitkv_splits(int B, int H, int N_q, int N_k, int d, int causal)
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
     int rc = check_device();
     if (rc != FA_OK) return rc;
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-        cus = 256;
+    int cus = 256, xcds = 8;
+    fa::device_geometry(cus, xcds);
     // Four workgroups per compute unit keep every unit busy with work queued
     // behind the resident ones (query tiles of the bf16 kernel).
     const double target = 4.0 * cus;
-    const int64_t bm = fa::query_tile_rows(FA_DTYPE_BF16, d, kSplitBlockN, B, H, N_q, causal ? 1 : 0, 1);
+    const int64_t bm =
+        fa::query_tile_rows(FA_DTYPE_BF16, d, kSplitBlockN, B, H, N_q, causal ? 1 : 0, 1, cus);
     const double wgs = (double)B * H * (((int64_t)N_q + bm - 1) / bm);
     if (wgs >= target) return 1;
     const int64_t keys = causal ? (N_q < N_k ? N_q : N_k) : N_k;

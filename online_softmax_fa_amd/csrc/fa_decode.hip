@@ -168,14 +168,33 @@ struct Decode {
 #pragma unroll
         for (int j = 0; j < 8; ++j) o[j] *= alpha;
         // o~ += p v: instruction i holds key i * KPI + g, whose weight is in
-        // lane (g, e = i) of this lane's group
+        // lane (g, e = i) of this lane's group.  A hidden key (masked, past
+        // N_k, a filler step) has weight exactly 0, but its V row may hold
+        // anything (padded cache slots, repeated rows), and 0 * NaN is NaN;
+        // when the step has such a weight its products are skipped instead,
+        // so hidden keys contribute exactly zero whatever their values.
+        if (__any(pv == 0.0f)) {
 #pragma unroll
-        for (int i = 0; i < C::NI; ++i) {
-            const float pk = __shfl(pv, i, C::LPK);
+            for (int i = 0; i < C::NI; ++i) {
+                const float pk = __shfl(pv, i, C::LPK);
+                const bool take = pk != 0.0f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                o[2 * j] = __builtin_fmaf(pk, lo_bf16(b.v[i][j]), o[2 * j]);
-                o[2 * j + 1] = __builtin_fmaf(pk, hi_bf16(b.v[i][j]), o[2 * j + 1]);
+                for (int j = 0; j < 4; ++j) {
+                    const float v0 = take ? lo_bf16(b.v[i][j]) : 0.0f;
+                    const float v1 = take ? hi_bf16(b.v[i][j]) : 0.0f;
+                    o[2 * j] = __builtin_fmaf(pk, v0, o[2 * j]);
+                    o[2 * j + 1] = __builtin_fmaf(pk, v1, o[2 * j + 1]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < C::NI; ++i) {
+                const float pk = __shfl(pv, i, C::LPK);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    o[2 * j] = __builtin_fmaf(pk, lo_bf16(b.v[i][j]), o[2 * j]);
+                    o[2 * j + 1] = __builtin_fmaf(pk, hi_bf16(b.v[i][j]), o[2 * j + 1]);
+                }
             }
         }
     }

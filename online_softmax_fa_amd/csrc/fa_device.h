@@ -22,11 +22,12 @@ static constexpr float kNegInf = -__builtin_inff();
 static constexpr float kLn2 = 0.693147180559945309f;
 
 // ---------------------------------------------------------------------------
-// Grid mapping.  Workgroups are dispatched round-robin over the 8 XCDs
-// (workgroup g runs on XCD g % 8), and each XCD takes its share in order of
-// g.  Work items are (batch-head, query tile, key range), key ranges
-// innermost.  Every XCD gets a contiguous range of them, so the query tiles of
-// one (batch, head) run on one XCD and share its L2 for K and V.
+// Grid mapping.  Workgroups are dispatched round-robin over the device's
+// XCDs (workgroup g runs on XCD g % X, X = Params.xcds, queried from the
+// device), and each XCD takes its share in order of g.  Work items are
+// (batch-head, query tile, key range), key ranges innermost.  Every XCD gets
+// a contiguous range of them, so the query tiles of one (batch, head) run on
+// one XCD and share its L2 for K and V.
 //
 // Under causality query tile t visits t + 1 times the keys of tile 0, so item
 // lengths differ, and a CU that finishes early takes the next item in
@@ -40,12 +41,12 @@ static constexpr float kLn2 = 0.693147180559945309f;
 // go head by head, each head's longest first.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int logical_tile(int g, int G, int n_qt, int n_split, bool causal,
-                                            int slots)
+                                            int slots, int X)
 {
-    const int x = g & 7, j = g >> 3;
+    const int x = g % X, j = g / X;
     const int heads = G / (n_qt * n_split);
-    if (causal && (heads & 7) == 0) {
-        const int hp = heads >> 3;                 // heads per XCD
+    if (causal && heads % X == 0) {
+        const int hp = heads / X;                  // heads per XCD
         const int items = n_qt * n_split;          // items per head
         int grp = 1;
         while (grp < hp && grp * items < slots) grp *= 2;
@@ -58,7 +59,7 @@ __device__ __forceinline__ int logical_tile(int g, int G, int n_qt, int n_split,
         const int hh = h0 + rest / n_split, sp = rest % n_split;
         return ((x * hp + hh) * n_qt + r) * n_split + sp;
     }
-    const int per = G >> 3, rem = G & 7;
+    const int per = G / X, rem = G % X;
     return x * per + (x < rem ? x : rem) + j;
 }
 

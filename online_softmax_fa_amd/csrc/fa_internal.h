@@ -36,12 +36,23 @@ struct Params {
     float *trace;
     int trace_bh;         // b * H + h of the traced row
     int trace_row;        // its query index
+    // Shape of the device, queried once per device by the entry points:
+    // compute units, and XCDs the dispatcher deals workgroups to in turn.
+    int cus;
+    int xcds;
 };
+
+// Compute units and XCDs of the current device (cached per device); 256 and
+// 8 when no device can be queried.  xcds is 1 unless it is a power of two
+// that divides cus (then workgroups are dealt to XCDs in turn).
+void device_geometry(int &cus, int &xcds);
 
 // Query rows per workgroup of the forward kernel for validated arguments
 // (dtype 0 = fp32, 1 = bf16; d 64 or 128; block_n 16, 32, 64 or 128; B, H,
-// n_q >= 1; n_split key ranges per query tile, 1 for the plain pass).
-int query_tile_rows(int dtype, int d, int block_n, int B, int H, int n_q, int causal, int n_split);
+// n_q >= 1; n_split key ranges per query tile, 1 for the plain pass; cus the
+// device's compute units).
+int query_tile_rows(int dtype, int d, int block_n, int B, int H, int n_q, int causal, int n_split,
+                    int cus);
 
 // Enqueues the forward kernel for validated arguments.  dtype: 0 = fp32,
 // 1 = bf16; d: 64 or 128; block_n: 16, 32, 64 or 128.

@@ -43,9 +43,18 @@
 
 #include <atomic>
 
+#include "fa.h"
 #include "fa_device.h"
 
 namespace fa {
+
+// The fast path of the bf16 kernels keeps a tile's weights against the
+// current exponent base when every lane's sum of them is at most
+// 2^FA_BF16_REF_LAG_LOG2 (include/fa.h): each weight is then at most that,
+// and the base lags the running maximum by less than FA_BF16_REF_LAG_LOG2
+// (log2 units).
+constexpr float kFastSumLimit = (float)(1u << FA_BF16_REF_LAG_LOG2);
+static_assert(FA_BF16_REF_LAG_LOG2 == 24, "the lag the documentation and tests state");
 
 // One step of the recurrence on a tile of raw scores held in s (NKB blocks of
 // 16 per lane), as the fp32 kernel runs it.  m_raw: running max in raw score
@@ -120,14 +129,13 @@ __device__ __forceinline__ bool lazy_step(f32x16 (&s)[NKB], bf16x8 (&pb)[NT16], 
 // is the critical path: causal workgroups differ in length (the last query
 // tile visits every key tile), so there it takes two per CU, which the
 // longest-first order packs evenly; equal-length non-causal ones need only
-// fill the CUs.  gfx950 parts have 256 CUs.
-constexpr int kComputeUnits = 256;
-
-inline int bf16_waves(int d, int bn, int64_t B, int64_t H, int64_t nq, bool causal, int n_split)
+// fill the CUs (the device's count, cus).
+inline int bf16_waves(int d, int bn, int64_t B, int64_t H, int64_t nq, bool causal, int n_split,
+                      int cus)
 {
     if (d != 128 || bn != 64 || nq <= 128) return 4;
     const int64_t wgs = B * H * ((nq + 255) / 256) * n_split;
-    return wgs >= (causal ? 2 : 1) * (int64_t)kComputeUnits ? 8 : 4;
+    return wgs >= (causal ? 2 : 1) * (int64_t)cus ? 8 : 4;
 }
 
 template <int D, int BN, int NW>
@@ -219,7 +227,7 @@ struct Bf16Fwd {
 
         // work item L = (head, query tile, key range), key ranges innermost
         const int L = logical_tile(blockIdx.x, gridDim.x, p.n_qt, p.n_split, CAUSAL,
-                                   kComputeUnits / 8 * bf16_blocks_per_cu<D, BN, NW>());
+                                   p.cus / p.xcds * bf16_blocks_per_cu<D, BN, NW>(), p.xcds);
         split = L % p.n_split;
         const int L2 = L / p.n_split;
         bh = L2 / p.n_qt;
@@ -391,6 +399,17 @@ struct Bf16Fwd {
 
         const int k0 = t * BN;
         const bool tile_empty = Mg && kv_lo == 0 && (BN <= 64 || kv_hi == 0);
+        // A masked key's weight is exactly 0, but the product P.V would still
+        // multiply it by the key's V row, and 0 * NaN or 0 * Inf is NaN:
+        // padded cache slots may hold anything.  On tiles with hidden keys
+        // (key-padding mask, or keys past N_k whose rows repeat the last
+        // key), those V rows are cleared in LDS first, so hidden keys
+        // contribute exactly zero whatever their values ("Pitfalls in
+        // implementing the recurrence"; the interview answer: masked keys
+        // contribute zero).  The mask is shared by all rows of the batch,
+        // so every wave can use the cleared rows.
+        if (Mg && !tile_empty && !(kv_lo == ~0ull && (BN <= 64 || kv_hi == ~0ull)))
+            clear_hidden_v<ST>();
         // Keys beyond this wave's last row are all masked under causality;
         // a wave whose rows all lie past N_q has nothing to compute.
         const bool wave_skip = tile_empty || (CAUSAL && k0 > qw0 + 31) || qw0 >= Nq;
@@ -401,6 +420,24 @@ struct Bf16Fwd {
             land();
             if (Mg) take_mask();
         }
+    }
+
+    // Zero the V rows of the keys of the tile in stage ST that the
+    // key-padding bits (kv_lo, kv_hi: visible and inside N_k) hide, then
+    // synchronise.  Rows are whole in LDS (the swizzle only permutes the
+    // 16-byte chunks inside a row).  Every thread of the workgroup calls it.
+    template <int ST>
+    __device__ __forceinline__ void clear_hidden_v()
+    {
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        for (int idx = threadIdx.x; idx < BN * C::CH; idx += C::T) {
+            const int row = idx / C::CH, ch = idx % C::CH;
+            const uint64_t word = row < 64 ? kv_lo : kv_hi;
+            if (!((word >> (row & 63)) & 1ull))
+                *reinterpret_cast<__attribute__((address_space(3))) u32x4 *>(
+                    lds + C::V_BASE + ST * C::TILE + row * C::ROW + 16 * ch) = zero;
+        }
+        __syncthreads();
     }
 
     // Raw scores S^T = K . Q^T of the tile in stage ST ("The math of
@@ -503,7 +540,7 @@ struct Bf16Fwd {
         bf16x8 pb[C::NT16];
         // Fast path: the weights against the current base, without the tile
         // maximum.  They are kept when every lane's sum of them is at most
-        // 2^24, which bounds each weight by 2^24 too; the base stays where it
+        // kFastSumLimit, which bounds each weight too; the base stays where it
         // is and alpha is 1.  Otherwise (a score far above the base, or a row
         // with no base yet, whose weights come out +inf or NaN and fail the
         // test) the scores are formed again from the K tile, which is still
@@ -521,7 +558,7 @@ struct Bf16Fwd {
                     fs[r & 3] += s[kb][r];
                 }
             tot = (fs[0] + fs[1]) + (fs[2] + fs[3]);
-            done = !__any(!(tot <= 16777216.0f));
+            done = !__any(!(tot <= kFastSumLimit));
             // the V reads first, then the vector work
             __builtin_amdgcn_sched_group_barrier(0x100, 2 * VA, 9);
             __builtin_amdgcn_sched_group_barrier(0x406, 512, 9);
@@ -750,7 +787,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_f32_kernel(const Params p)
 
     // work item L = (head, query tile, key range), key ranges innermost
     const int L = logical_tile(blockIdx.x, gridDim.x, p.n_qt, p.n_split, CAUSAL,
-                               kComputeUnits / 8 * 2);
+                               p.cus / p.xcds * 2, p.xcds);
     const int split = L % p.n_split;
     const int L2 = L / p.n_split;
     const int bh = L2 / p.n_qt;
@@ -858,6 +895,17 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_f32_kernel(const Params p)
             }
         }
         const bool tile_empty = Mg && kv_lo == 0 && (BN <= 64 || kv_hi == 0);
+        // V rows of hidden keys are cleared before the products, so that
+        // their zero weights never meet non-finite values (as in the bf16
+        // kernel).
+        if (Mg && !tile_empty && !(kv_lo == ~0ull && (BN <= 64 || kv_hi == ~0ull))) {
+            for (int x = tid; x < BN * D; x += C::T) {
+                const int row = x / D;
+                const uint64_t word = row < 64 ? kv_lo : kv_hi;
+                if (!((word >> (row & 63)) & 1ull)) Vl[row * C::P + x % D] = 0.0f;
+            }
+            __syncthreads();
+        }
         if (!(tile_empty || (CAUSAL && k0 > qw0 + 31) || qw0 >= Nq))
             f32_tile<D, BN, NW, CAUSAL>(Kl, Vl, qf, k0, Nk, qw0, qrow, l31, h, Mg, kv_lo, kv_hi, c,
                                         m_raw, l_part, o);
@@ -952,7 +1000,7 @@ template <int D, int BN>
 static hipError_t dispatch_bf16(const Params &p, int causal, int B, int H, hipStream_t stream)
 {
     if constexpr (D == 128 && BN == 64) {
-        if (bf16_waves(D, BN, B, H, p.Nq, causal != 0, p.n_split) == 8)
+        if (bf16_waves(D, BN, B, H, p.Nq, causal != 0, p.n_split, p.cus) == 8)
             return dispatch_bf16_nw<D, BN, 8>(p, causal, B, H, stream);
     }
     return dispatch_bf16_nw<D, BN, 4>(p, causal, B, H, stream);
@@ -989,9 +1037,10 @@ static hipError_t dispatch_d(const Params &p, int dtype, int block_n, int causal
     }
 }
 
-int query_tile_rows(int dtype, int d, int block_n, int B, int H, int n_q, int causal, int n_split)
+int query_tile_rows(int dtype, int d, int block_n, int B, int H, int n_q, int causal, int n_split,
+                    int cus)
 {
-    return dtype == 1 ? 32 * bf16_waves(d, block_n, B, H, n_q, causal != 0, n_split) : 32 * 4;
+    return dtype == 1 ? 32 * bf16_waves(d, block_n, B, H, n_q, causal != 0, n_split, cus) : 32 * 4;
 }
 
 hipError_t launch_fwd(const Params &p, int dtype, int d, int block_n, int causal, int B, int H,

@@ -18,6 +18,18 @@ import oracle
 import online_softmax_fa_amd as fa
 
 TOL = {"f32": dict(max_abs=1e-5, mean_abs=None), "bf16": dict(max_abs=2e-2, mean_abs=2e-3)}
+
+
+def header_define(name):
+    """The integer value of a #define in include/fa.h (the bounds the library
+    documents are read from the header, not restated)."""
+    import os
+    import re
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                        "fa.h")
+    m = re.search(r"^#define\s+%s\s+(\d+)\s*$" % name, open(path).read(), re.M)
+    assert m, name
+    return int(m.group(1))
 LSE_TOL = 1e-3
 
 

@@ -90,7 +90,7 @@ def test_pages_toy_rows(bn):
     o, lse = run_gpu(q, k, v, 1.0, block_n=bn)
     assert abs(o[0, 0, 0, 0] - 36.88) <= 5e-3
     o_ref, lse_ref = run_oracle(q, k, v, 1.0)
-    compare(o, lse, o_ref, lse_ref, "f32", max_abs=1e-5 * 40, what="toy2 bn%d" % bn)
+    compare(o, lse, o_ref, lse_ref, "f32", what="toy2 bn%d" % bn)    # the plain 1e-5 bar
 
     q, k, v = _toy_tensors([1, 2, 5, 3], [[1, 0], [0, 1], [2, 0], [0, 2]])
     o, lse = run_gpu(q, k, v, 1.0, block_n=bn)

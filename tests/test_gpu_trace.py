@@ -21,7 +21,9 @@ import torch
 from oracle.online import online_attention_row
 from online_softmax_fa_amd import inputs
 import online_softmax_fa_amd as fa
-from _parity import say, to_np32
+from _parity import header_define, say, to_np32
+
+LAG_LOG2 = header_define("FA_BF16_REF_LAG_LOG2")
 
 pytestmark = pytest.mark.gpu
 
@@ -118,8 +120,9 @@ def test_trace_of_adversarial_rows(dtype, bn, rev):
                         m_true = e["m_new"] / scale
                         slack = 1e-6 * abs(m_true) + 1e-6         # rounding of mc / c
                         assert m <= m_true + slack
-                        # lag bound: the fast path keeps weights up to 2^24
-                        assert m >= m_true - 24.0 / c - slack
+                        # lag bound of the header: the fast path keeps weights
+                        # up to 2^FA_BF16_REF_LAG_LOG2
+                        assert m >= m_true - LAG_LOG2 / c - slack
                     assert abs(lse_k - lse_o) <= 1e-5 * max(1.0, abs(lse_o))
 
 
