@@ -38,8 +38,19 @@ static constexpr float kLn2 = 0.693147180559945309f;
 // least as many items as the XCD runs workgroups at once (`slots`), which
 // keeps the K/V the XCD reads at a time, and so its L2 footprint, small.
 // That needs the heads to divide evenly among the XCDs; otherwise the items
-// go head by head, each head's longest first.
+// go head by head, each head's longest first.  When pairs of query tiles
+// (t, n_qt - 1 - t) fill whole rounds of the device's workgroup slots, the
+// bf16 launcher pairs them instead (pair_item), which needs no ordering.
 // ---------------------------------------------------------------------------
+// Workgroups g = 0 .. G-1 dealt to X XCDs in turn, numbered so that every
+// XCD holds a contiguous range of the G items.
+__device__ __forceinline__ int xcd_contiguous(int g, int G, int X)
+{
+    const int x = g % X, j = g / X;
+    const int per = G / X, rem = G % X;
+    return x * per + (x < rem ? x : rem) + j;
+}
+
 __device__ __forceinline__ int logical_tile(int g, int G, int n_qt, int n_split, bool causal,
                                             int slots, int X)
 {
@@ -59,8 +70,26 @@ __device__ __forceinline__ int logical_tile(int g, int G, int n_qt, int n_split,
         const int hh = h0 + rest / n_split, sp = rest % n_split;
         return ((x * hp + hh) * n_qt + r) * n_split + sp;
     }
-    const int per = G / X, rem = G % X;
-    return x * per + (x < rem ? x : rem) + j;
+    return xcd_contiguous(g, G, X);
+}
+
+// Work item of workgroup g when causal query tiles go in pairs: the
+// workgroup takes query tiles n_qt - 1 - t and t of one (batch, head), the
+// longer first ("2.2b", "Scaling to Multiple Queries": rows are independent,
+// so one workgroup may take any of them).  Every pair visits the same number
+// of key tiles (an odd n_qt's middle tile is alone and shorter), so the
+// workgroups are equally long and need no ordering; pairs are dealt to the
+// XCDs in contiguous ranges (a head stays on one XCD).  item: 0 or 1;
+// returns false when the workgroup has no such item.
+__device__ __forceinline__ bool pair_item(int g, int G, int n_qt, int X, int item, int &bh,
+                                          int &qt)
+{
+    const int np = (n_qt + 1) / 2;
+    const int L = xcd_contiguous(g, G, X);
+    bh = L / np;
+    const int t = L - bh * np;
+    qt = item == 0 ? n_qt - 1 - t : t;
+    return item == 0 || t != n_qt - 1 - t;
 }
 
 // Position, inside a 32-key block, of register r of a lane with half h = l/32:

@@ -40,6 +40,9 @@ struct Params {
     // compute units, and XCDs the dispatcher deals workgroups to in turn.
     int cus;
     int xcds;
+    // Causal query tiles go in pairs (t, n_qt - 1 - t), two work items per
+    // workgroup; set by the launcher of the bf16 kernel.
+    int pair;
 };
 
 // Compute units and XCDs of the current device (cached per device); 256 and

@@ -214,7 +214,28 @@ struct Bf16Fwd {
     uint64_t kv_lo, kv_hi;
     int mnext0, mnext1;     // key-padding bytes of the next tile
 
-    __device__ __forceinline__ void init(const Params &p, lds_char *lds_base)
+    // Work item `item` of this workgroup (0, or 1 when causal query tiles go
+    // in pairs): (batch-head, query tile, key range).  False if there is none.
+    static __device__ __forceinline__ bool work_item(const Params &p, int item, int &bh_, int &qt,
+                                                     int &split_)
+    {
+        if (CAUSAL && p.pair) {
+            split_ = 0;
+            return pair_item(blockIdx.x, gridDim.x, p.n_qt, p.xcds, item, bh_, qt);
+        }
+        if (item > 0) return false;
+        // L = (head, query tile, key range), key ranges innermost
+        const int L = logical_tile(blockIdx.x, gridDim.x, p.n_qt, p.n_split, CAUSAL,
+                                   p.cus / p.xcds * bf16_blocks_per_cu<D, BN, NW>(), p.xcds);
+        split_ = L % p.n_split;
+        const int L2 = L / p.n_split;
+        bh_ = L2 / p.n_qt;
+        qt = CAUSAL ? (p.n_qt - 1 - L2 % p.n_qt) : (L2 % p.n_qt);
+        return true;
+    }
+
+    __device__ __forceinline__ void init(const Params &p, lds_char *lds_base, int bh_, int qt,
+                                         int split_)
     {
         lds = lds_base;
         const int tid = threadIdx.x;
@@ -225,13 +246,8 @@ struct Bf16Fwd {
         l31 = lane & 31;
         h = lane >> 5;
 
-        // work item L = (head, query tile, key range), key ranges innermost
-        const int L = logical_tile(blockIdx.x, gridDim.x, p.n_qt, p.n_split, CAUSAL,
-                                   p.cus / p.xcds * bf16_blocks_per_cu<D, BN, NW>(), p.xcds);
-        split = L % p.n_split;
-        const int L2 = L / p.n_split;
-        bh = L2 / p.n_qt;
-        const int qt = CAUSAL ? (p.n_qt - 1 - L2 % p.n_qt) : (L2 % p.n_qt);
+        split = split_;
+        bh = bh_;
         b = bh / p.H;
         q0 = qt * C::BM;
         qw0 = q0 + 32 * w;          // first query row of this wave
@@ -598,6 +614,23 @@ struct Bf16Fwd {
         }
     }
 
+    // The whole pass over one work item: state, the tile loop, the epilogue.
+    __device__ __forceinline__ void run(const Params &p, lds_char *lds_base, int bh_, int qt,
+                                        int split_)
+    {
+        init(p, lds_base, bh_, qt, split_);
+
+        if (n_t > 0) fetch(0, 0);
+        land();
+        if (Mg) take_mask();
+
+        for (int it = 0; it < n_t; it += 2) {
+            iteration<0>(it);
+            if (it + 1 < n_t) iteration<1>(it + 1);
+        }
+        epilogue(p);
+    }
+
     // The reference of the row's state in raw score units: mc / c.
     __device__ __forceinline__ float m_raw() const { return mc == kNegInf ? kNegInf : mc / c; }
 
@@ -667,18 +700,18 @@ __global__ __launch_bounds__(NW * 64, (bf16_blocks_per_cu<D, BN, NW>())) void fa
     const Params p)
 {
     extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
-    Bf16Fwd<D, BN, NW, CAUSAL, TRACE> k;
-    k.init(p, (lds_char *)lds_raw);
-
-    if (k.n_t > 0) k.fetch(0, 0);
-    k.land();
-    if (k.Mg) k.take_mask();
-
-    for (int it = 0; it < k.n_t; it += 2) {
-        k.template iteration<0>(it);
-        if (it + 1 < k.n_t) k.template iteration<1>(it + 1);
+    using F = Bf16Fwd<D, BN, NW, CAUSAL, TRACE>;
+    F k;
+    int bh, qt, split;
+    F::work_item(p, 0, bh, qt, split);
+    k.run(p, (lds_char *)lds_raw, bh, qt, split);
+    // The second item of a pair, after a barrier: the first item's last tile
+    // may still be read from LDS.  (Written out rather than as a loop, which
+    // would keep the first item's registers live across both.)
+    if (CAUSAL && F::work_item(p, 1, bh, qt, split)) {
+        __syncthreads();
+        k.run(p, (lds_char *)lds_raw, bh, qt, split);
     }
-    k.epilogue(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -992,7 +1025,15 @@ static hipError_t dispatch_bf16_nw(const Params &p0, int causal, int B, int H, h
     using C = Bf16Cfg<D, BN, NW>;
     Params p = p0;
     p.n_qt = (p.Nq + C::BM - 1) / C::BM;
-    const int grid = B * H * p.n_qt * p.n_split;
+    // Under causality the query tiles of a head differ in length (tile t
+    // visits t + 1 times the keys of tile 0); paired as (t, n_qt - 1 - t)
+    // they make workgroups of one length, which finish together when they
+    // fill whole rounds of the device's workgroup slots.  Otherwise (or when
+    // a round would be only partly full) the items go singly, longest first.
+    const int64_t pairs = (int64_t)B * H * ((p.n_qt + 1) / 2);
+    const int64_t slots = (int64_t)p.cus * bf16_blocks_per_cu<D, BN, NW>();
+    p.pair = causal && p.n_split == 1 && p.n_qt >= 2 && pairs % slots == 0;
+    const int grid = p.pair ? (int)pairs : B * H * p.n_qt * p.n_split;
     return launch_variant<D, BN, NW, true>(causal, grid, C::T, C::LDS_BYTES, stream, p);
 }
 

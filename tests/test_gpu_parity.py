@@ -246,6 +246,44 @@ def test_256_row_workgroups(shape):
         assert np.all(o.reshape(B, H, Nq, d)[1] == 0.0) and np.all(np.isneginf(lse[1]))
 
 
+# ---------------------------------------------------------------------------
+# Paired causal query tiles: when the pairs (t, n_qt - 1 - t) of a causal
+# launch fill whole rounds of the device's workgroup slots (256 CUs: one
+# 8-wave workgroup or three d = 64 workgroups per CU), each workgroup takes
+# both tiles of a pair one after the other.  An odd n_qt leaves the middle
+# tile alone.
+# ---------------------------------------------------------------------------
+PAIRED = [
+    # (B, H, Nq, d, masked): 8 waves, n_qt = 31 (ragged, odd), 2*16*16 = 512 pairs
+    (2, 16, 7700, 128, True),
+    # 4 waves of d = 64, n_qt = 32, 48*16 = 768 pairs
+    (1, 48, 4096, 64, False),
+]
+
+
+@pytest.mark.parametrize("shape", PAIRED, ids=["%dx%dx%dx%d%s" % (s[:4] + ("m" if s[4] else "",))
+                                              for s in PAIRED])
+def test_paired_causal_tiles(shape):
+    B, H, Nq, d, masked = shape
+    seed = 5900 + H
+    q, k, v = inputs.gaussian_qkv(B, H, Nq, Nq, d, seed, 1.0, "bf16")
+    mask = None
+    if masked:
+        lens = inputs.kv_lengths(B, Nq, seed + 1)
+        mask = inputs.prefix_mask(lens, Nq)
+    scale = inputs.default_scale(d)
+    heads = [(0, 0), (B - 1, H - 1), (B - 1, H // 2)]
+    rows = sample_rows(B, H, Nq, heads, 256, seed + 2)
+    rows = np.unique(np.concatenate([rows, np.arange(Nq) + (H // 3) * Nq]))   # one head in full
+    o_ref, lse_ref = run_oracle(q, k, v, scale, causal=True, mask=mask, rows=rows)
+    for rev in (False, True):
+        say("paired causal tiles %s reverse=%d" % (shape, rev))
+        o, lse = run_gpu(q, k, v, scale, causal=True, mask=mask, reverse_kv=rev)
+        compare(o.reshape(-1, d)[rows], lse.reshape(-1)[rows], o_ref, lse_ref, "bf16",
+                what="paired rev%d" % rev)
+        assert np.all(np.isfinite(o))
+
+
 def _span_mask(N):
     """Key-padding masks whose visible keys sit inside the key range, so that
     whole key tiles before and after them are skipped: batch 0 sees keys
