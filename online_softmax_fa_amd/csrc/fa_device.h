@@ -220,10 +220,17 @@ __device__ __forceinline__ int swz_v(int r)
 // all DMA in flight.  The kernel orders the two itself: a stage is read only
 // after the s_waitcnt vmcnt(0) and barrier that end the iteration filling it,
 // and refilled only after the barrier that ends the iteration reading it.
+// The base address is first copied by a scalar move: gfx9 needs five wait
+// states between a VALU instruction writing an SGPR (as v_readlane does when
+// the compiler restores a spilled base right before the asm, whose contents
+// it does not inspect) and a vector-memory instruction reading it, while a
+// scalar instruction reading it waits in hardware.  The move also gives the
+// one wait state after the M0 write.
 __device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds_addr)
 {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :
+    uint64_t b;
+    asm volatile("s_mov_b64 %0, %2\n\tglobal_load_lds_dwordx4 %1, %0"
+                 : "=&s"(b)
                  : "v"(voff), "s"(base), "{m0}"(lds_addr));
 }
 

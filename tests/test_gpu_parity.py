@@ -254,7 +254,10 @@ def test_256_row_workgroups(shape):
 # tile alone.
 # ---------------------------------------------------------------------------
 PAIRED = [
-    # (B, H, Nq, d, masked): 8 waves, n_qt = 31 (ragged, odd), 2*16*16 = 512 pairs
+    # (B, H, Nq, d, masked): 8 waves, n_qt = 31 (ragged, odd), 2*16*16 = 512 pairs;
+    # unmasked, the second item's first key tile is fetched during the first
+    # item's last tile whenever the first item has an even tile count
+    (2, 16, 7700, 128, False),
     (2, 16, 7700, 128, True),
     # 4 waves of d = 64, n_qt = 32, 48*16 = 768 pairs
     (1, 48, 4096, 64, False),
