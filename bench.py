@@ -151,7 +151,8 @@ def counters_from_profile(workload):
     if t.get("kernel_source_sha256_16") != kernel_source_hash(workload):
         return None
     return {k: t[k] for k in ("mfma_busy_pct", "valu_issue_pct", "lds_bank_conflicts",
-                              "exp2_per_mfma", "hbm_gb_per_s", "sustained_clock_ghz") if k in t}
+                              "exp2_per_mfma", "hbm_gb_per_s", "sustained_clock_ghz",
+                              "cu_busy_pct") if k in t}
 
 
 def cpu_baseline(w, seconds):

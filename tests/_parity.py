@@ -92,7 +92,25 @@ def compare(o, lse, o_ref, lse_ref, dt, max_abs=None, mean_abs=None, lse_tol=LSE
         assert stats["lse_max_abs"] <= lse_tol, "%s: max |lse - ref| = %.3e > %.1e" % (
             what, stats["lse_max_abs"], lse_tol)
     say("  %s: %s" % (what, ", ".join("%s=%.3e" % kv for kv in stats.items())))
+    log_margins(what, dt, stats, max_abs, mean_abs, lse_tol, int(live.sum()), int(dead.sum()))
     return stats
+
+
+def log_margins(what, dt, stats, max_abs, mean_abs, lse_tol, rows, dead_rows):
+    """With FA_PARITY_LOG set, append one JSON line per comparison (the test,
+    the case, the achieved errors and the bars) to that file: the source of
+    the committed per-configuration margin summary."""
+    import json
+    import os
+    path = os.environ.get("FA_PARITY_LOG")
+    if not path:
+        return
+    rec = {"test": os.environ.get("PYTEST_CURRENT_TEST", "").rsplit(" ", 1)[0], "case": what,
+           "dtype": dt, "rows": rows, "rows_without_visible_key": dead_rows,
+           "bars": {"max_abs": max_abs, "mean_abs": mean_abs, "lse_max_abs": lse_tol}}
+    rec.update(stats)
+    with open(path, "a") as fh:
+        fh.write(json.dumps(rec) + "\n")
 
 
 def sample_rows(B, H, N, heads, n_random, seed):
