@@ -115,6 +115,17 @@ typedef enum fa_dtype {
  * The pages require such rows to have a defined convention instead of 0/0
  * (tiled-attention interview answer, second paragraph) without naming one;
  * this is the library's.
+ *
+ * Non-finite inputs.  Keys that kv_len_mask hides contribute exactly zero
+ * whatever their k and v rows hold, NaN and +-inf included (padded cache
+ * slots may hold anything): their scores become -inf by selection before
+ * the tile maximum, and their v rows never enter a product.  Key j, which
+ * the causal mask hides from the rows i < j, is visible to the rows i >= j:
+ * a non-finite k or v row of it is a non-finite input of those rows, and
+ * through its zero weight inside the matrix product of the key tile on the
+ * diagonal it may also turn rows i < j of that tile non-finite.  Every
+ * other non-finite value in q, k or v propagates as the definition makes
+ * it.
  */
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
            int B, int H, int N_q, int N_k, int d, float scale, int causal,
