@@ -199,15 +199,16 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
               const fa_opts *opts);
 
 /*
- * fa_query_tile_rows -- query rows one workgroup of fa_fwd / fa_fwd_ex
- * processes for these arguments (block_n as in fa_opts, 0 = library choice;
- * causal nonzero or 0): the rows that share each key/value tile staged in
- * on-chip memory, since query rows are independent ("2.2b", "Scaling to
- * Multiple Queries").  128 or 256; the library takes 256 only for bfloat16,
- * d = 128, 64-key tiles, N_q > 128 and enough workgroups to fill the GPU
- * without one long causal workgroup deciding the run time.  Under causality
- * a workgroup visits the key tiles up to the diagonal of the last row of its
- * query tile, so a trace has one entry per such tile.  Returns the row
+ * fa_query_tile_rows -- query rows of one query tile of fa_fwd / fa_fwd_ex
+ * for these arguments (block_n as in fa_opts, 0 = library choice; causal
+ * nonzero or 0): the rows that share each key/value tile staged in on-chip
+ * memory, since query rows are independent ("2.2b", "Scaling to Multiple
+ * Queries").  128 or 256; the library takes 256 only for bfloat16, d = 128,
+ * 64-key tiles, N_q > 128 and enough query tiles to fill the GPU without one
+ * long causal tile deciding the run time.  (A workgroup may take two query
+ * tiles of a head in turn; that does not change what a tile visits.)  Under
+ * causality a query tile visits the key tiles up to the diagonal of its last
+ * row, so a trace has one entry per such tile.  Returns the row
  * count, or FA_ERR_SHAPE (B, H or N_q < 1) / FA_ERR_HEAD_DIM / FA_ERR_DTYPE /
  * FA_ERR_TILE.  Besides its arguments it depends only on the current
  * device's compute-unit count ("enough workgroups"), queried once per device;
