@@ -156,3 +156,38 @@ def test_trace_leaves_the_result_unchanged(dtype):
     o0, lse0 = fa.attention(qd, kd, vd, scale=scale, causal=True)
     _, o1, lse1 = _trace(qd, kd, vd, scale, True, None, 64, False, 1, 2, 150)
     assert torch.equal(o0, o1) and torch.equal(lse0, lse1)
+
+
+def test_trace_in_paired_workgroups():
+    """Causal bf16 launch whose 256-row query tiles go in pairs (t, n-1-t), one
+    workgroup taking both in turn (B=4 H=256 N=257 d=128: 1024 pairs on 256
+    CUs): the trace of a row in the first item of a pair (tile 1) and in the
+    second (tile 0) follows the oracle's recurrence, and tracing leaves the
+    result unchanged."""
+    B, H, N, d = 4, 256, 257, 128
+    q, k, v = inputs.gaussian_qkv(B, H, N, N, d, seed=2990, dtype="bf16")
+    scale = inputs.default_scale(d)
+    c = scale * LOG2E
+    qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+    bm = fa.fa_query_tile_rows(fa.FA_DTYPE_BF16, B, H, N, d, 64, True)
+    o0, lse0 = fa.attention(qd, kd, vd, scale=scale, causal=True)
+    for b, h, row in ((0, 0, 0), (1, 7, 200), (2, 100, 256), (3, 255, 255)):
+        say("paired trace b %d h %d row %d" % (b, h, row))
+        tr, o1, lse1 = _trace(qd, kd, vd, scale, True, None, 64, False, b, h, row)
+        assert torch.equal(o0, o1) and torch.equal(lse0, lse1)
+        t0, n_t = _tiles_visited(row, N, 64, True, bm)
+        assert np.all(np.isfinite(tr[:n_t, 0])) and np.all(np.isnan(tr[n_t:]))
+        qn = to_np32(q[b, h]).astype(np.float64)
+        kn = to_np32(k[b, h]).astype(np.float64)
+        s_row = scale * (kn @ qn[row])
+        vis = np.arange(N) <= row
+        ref = _oracle_trace(s_row, vis, 64, t0, n_t, False)["trace"]
+        assert [int(t) for t in tr[:n_t, 0]] == [e["block"] for e in ref]
+        for e, (t, m, l, _) in zip(ref, tr[:n_t]):
+            if e["m_new"] == -math.inf:
+                assert m == -math.inf and l == 0.0
+                continue
+            m_true = e["m_new"] / scale
+            slack = 1e-6 * abs(m_true) + 1e-6
+            assert m_true - LAG_LOG2 / c - slack <= m <= m_true + slack
+            assert abs(m * scale + math.log(l) - (e["m_new"] + math.log(e["l"]))) <= 1e-3
