@@ -15,7 +15,8 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
              timed region (`value` and ms_per_step are the mean of the K)
   counters   matrix-core busy %, vector issue %, LDS bank conflicts and HBM
              GB/s of the kernel, from the committed rocprofv3 summary
-             (profiles/), while it matches the kernel source; else null
+             (profiles/), while it was taken on the kernel code in the built
+             library; else null
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
              workload's rows, on this host's cores, in the same unit
   parity     the last launch's o and lse on those sample rows against the
@@ -44,6 +45,7 @@ import argparse
 import hashlib
 import json
 import os
+import struct
 import sys
 import time
 
@@ -59,21 +61,84 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# Sources that decide the HBM traffic of each workload's kernels: a stored
-# counter summary is used only while these files are unchanged.
-TRAFFIC_SOURCES = {
-    "softmax": ("fa_softmax.hip", "fa_internal.h"),
-    "decode": ("fa_decode.hip", "fa_kernels.hip", "fa_device.h", "fa_internal.h"),
+# Kernels whose machine code decides each workload's counters and HBM
+# traffic (substrings of their symbol names in the gfx950 code objects of
+# libfa.so).  A stored counter summary is used only while that code is the
+# code it was taken on: comments and unrelated kernels do not invalidate it,
+# a change of source, compiler or flags that changes the code does.
+PROFILED_KERNELS = {
+    "headline": ("fa_fwd_bf16_kernelILi128ELi64ELi8ELb1ELb0E",),
+    "long": ("fa_fwd_bf16_kernelILi128ELi64ELi8ELb0ELb0E",),
+    "mid": ("fa_fwd_bf16_kernelILi64ELi64ELi4ELb1ELb0E",),
+    "decode": ("fa_decode_bf16_kernelILi128E", "fa_merge_kernelILi128E"),
+    "softmax": ("fa_softmax_rows_kernel",),
 }
-DEFAULT_TRAFFIC_SOURCES = ("fa_kernels.hip", "fa_device.h", "fa_internal.h")
+_BUNDLE_MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
 
 
-def kernel_source_hash(workload):
-    h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES.get(workload, DEFAULT_TRAFFIC_SOURCES):
-        with open(os.path.join(ROOT, "online_softmax_fa_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+def _elf_sections(d):
+    """[(name, addr, offset, size, type, link)] of a 64-bit little-endian ELF image."""
+    shoff = struct.unpack_from("<Q", d, 0x28)[0]
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", d, 0x3A)
+    raw = [struct.unpack_from("<IIQQQQIIQQ", d, shoff + i * shentsize) for i in range(shnum)]
+    stroff = raw[shstrndx][4]
+    return [(d[stroff + r[0]: d.index(b"\0", stroff + r[0])].decode(), r[3], r[4], r[5], r[1], r[6])
+            for r in raw]
+
+
+def device_kernels(lib_path, arch="gfx950"):
+    """{symbol name: machine code} of every function in lib_path's device
+    code objects for arch (clang offload bundles in its .hip_fatbin section)."""
+    with open(lib_path, "rb") as fh:
+        d = fh.read()
+    fat = next((d[o:o + n] for (nm, a, o, n, t, l) in _elf_sections(d) if nm == ".hip_fatbin"), b"")
+    kernels = {}
+    pos = fat.find(_BUNDLE_MAGIC)
+    while pos >= 0:
+        q = pos + len(_BUNDLE_MAGIC) + 8
+        for _ in range(struct.unpack_from("<Q", fat, pos + len(_BUNDLE_MAGIC))[0]):
+            off, size, idlen = struct.unpack_from("<QQQ", fat, q)
+            ident = fat[q + 24: q + 24 + idlen].decode()
+            q += 24 + idlen
+            if not ident.endswith(arch):
+                continue
+            co = fat[pos + off: pos + off + size]
+            secs = _elf_sections(co)
+            for (nm, a, o, sz, t, link) in secs:
+                if t != 2:                                   # SHT_SYMTAB
+                    continue
+                stro = secs[link][2]
+                for k in range(sz // 24):
+                    st_name, st_info, _, st_shndx, st_value, st_size = \
+                        struct.unpack_from("<IBBHQQ", co, o + 24 * k)
+                    if st_info & 0xF != 2 or st_size == 0:     # STT_FUNC
+                        continue
+                    name = co[stro + st_name: co.index(b"\0", stro + st_name)].decode()
+                    sec = secs[st_shndx]
+                    start = sec[2] + st_value - sec[1]
+                    kernels[name] = co[start: start + st_size]
+        pos = fat.find(_BUNDLE_MAGIC, pos + len(_BUNDLE_MAGIC))
+    return kernels
+
+
+_CODE_HASHES = {}
+
+
+def kernel_code_hash(workload):
+    """First 16 hex digits of the SHA-256 of the workload's kernels' names and
+    machine code in the built libfa.so, or None if they cannot be read."""
+    if workload not in _CODE_HASHES:
+        try:
+            ks = device_kernels(os.path.join(ROOT, "online_softmax_fa_amd", "libfa.so"))
+            names = sorted(n for n in ks if any(p in n for p in PROFILED_KERNELS[workload]))
+            h = hashlib.sha256()
+            for n in names:
+                h.update(n.encode())
+                h.update(ks[n])
+            _CODE_HASHES[workload] = h.hexdigest()[:16] if names else None
+        except (OSError, KeyError, ValueError, struct.error, IndexError):
+            _CODE_HASHES[workload] = None
+    return _CODE_HASHES[workload]
 
 
 def attention_flops(B, H, Nq, Nk, d, causal):
@@ -128,13 +193,14 @@ def algorithmic_bytes(B, H, Nq, Nk, d, esz):
 
 def traffic_from_profile(workload):
     """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel source; else None."""
+    taken on the kernel code in the built library; else None."""
     path = os.path.join(ROOT, "profiles", "%s_hbm_traffic.json" % workload)
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         t = json.load(fh)
-    if t.get("kernel_source_sha256_16") != kernel_source_hash(workload):
+    code = kernel_code_hash(workload)
+    if code is None or t.get("kernel_code_sha256_16") != code:
         return None
     return t.get("bytes_per_launch")
 
@@ -142,13 +208,15 @@ def traffic_from_profile(workload):
 def counters_from_profile(workload):
     """Hardware counters of the dominant kernel from the committed rocprofv3
     summary (matrix-core busy %, vector issue %, LDS bank conflicts, HBM
-    GB/s), if they were taken on the current kernel source; else None."""
+    GB/s), if they were taken on the kernel code in the built library; else
+    None."""
     path = os.path.join(ROOT, "profiles", "%s_counters.json" % workload)
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         t = json.load(fh)
-    if t.get("kernel_source_sha256_16") != kernel_source_hash(workload):
+    code = kernel_code_hash(workload)
+    if code is None or t.get("kernel_code_sha256_16") != code:
         return None
     return {k: t[k] for k in ("mfma_busy_pct", "valu_issue_pct", "lds_bank_conflicts",
                               "exp2_per_mfma", "hbm_gb_per_s", "sustained_clock_ghz",

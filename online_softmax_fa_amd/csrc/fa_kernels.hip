@@ -15,12 +15,14 @@
 // FlashAttention", end of "The block-wise update").  Both products run on the
 // CDNA4 matrix cores.
 //
-// Work decomposition (one workgroup = NW waves = 32*NW query rows of one
-// (batch, head)):
-//   - each wave owns 32 query rows for the whole kernel;
-//   - key/value tiles of BN keys are staged in LDS, double-buffered, from
-//     16-byte global loads; V is written transposed (key index fastest) so the
-//     P.V operand reads are contiguous;
+// Work decomposition (one work item = NW waves = 32*NW query rows of one
+// (batch, head); a workgroup takes one item, or two when causal query tiles
+// go in pairs):
+//   - each wave owns 32 query rows for the whole item;
+//   - key/value tiles of BN keys are staged in LDS, double-buffered, by LDS
+//     DMA of 16 bytes per lane, both in [key][dim] order with XOR-permuted
+//     16-byte chunks; the P.V operands come out of V through transposing LDS
+//     reads;
 //   - scores are formed transposed, S^T = K . Q^T, with the 32x32 MFMA: lane l
 //     then holds 16 keys of ONE query row (row l % 32), so the row maximum and
 //     row sum are in-lane reductions plus one exchange with lane l ^ 32, and

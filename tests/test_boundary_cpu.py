@@ -293,3 +293,31 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def _bench_module():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("fa_bench", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_bench_reads_kernel_code_from_the_library():
+    """bench.py keys the committed counter summaries by the machine code of
+    each workload's kernels, read from the gfx950 code objects in libfa.so:
+    every profiled workload finds its kernels there, and the hash depends on
+    the code alone."""
+    if not os.path.exists(fa.LIB_PATH):
+        pytest.fail("libfa.so is not built; run __graft_entry__.build()")
+    b = _bench_module()
+    ks = b.device_kernels(fa.LIB_PATH)
+    assert ks, "no gfx950 device functions found in libfa.so"
+    for workload, patterns in b.PROFILED_KERNELS.items():
+        for p in patterns:
+            assert any(p in n for n in ks), (workload, p)
+        h = b.kernel_code_hash(workload)
+        assert h is not None and len(h) == 16 and int(h, 16) >= 0
+    # every kernel is whole machine code: a multiple of the 4-byte instruction unit
+    assert all(len(code) % 4 == 0 and len(code) > 0 for code in ks.values())
+    assert b.kernel_code_hash("headline") != b.kernel_code_hash("long")
